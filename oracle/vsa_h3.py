@@ -1,0 +1,367 @@
+"""Plain, slow CPU definition of the VSA-H3 attention forward (NumPy).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): never called by the
+product path.
+
+What is computed, and where the pages state it
+----------------------------------------------
+The normative description is the VSA-H3 paragraph of "FastH3 4-step Preview
+(VSA, data-free)", section "Video Sparse Attention is not optional here":
+video tokens are cut into 64-token (4, 4, 4) tiles over the post-patchify
+grid; the conditioning prefix is cut into tiles that never mix segments;
+per-head fp32 tile scores come from pooled q and k; every video query tile
+keeps the top ``topk = max(1, min(ceil((1 - sparsity) * n_video_tiles),
+n_video_tiles))`` video key tiles; prefix key tiles are always kept and prefix
+query tiles attend to everything; a compression branch ``softmax(scores) @
+pool(v)`` is broadcast over each query tile's rows and scaled by a gate with
+no activation; the tile geometry is derived from token tags and positions.
+Supporting passages: "FastH3 NVFP4 on RTX PRO 6000 (sm_120)", section
+"Block-sparse FP4 attention for VSA tiles" (per-query-block lists of key
+blocks, partially filled tiles, every query visits prefix block 0) and
+section "Model integration" (gather into tile order with zero pad rows,
+gather back to packed order; the gate is applied per token after the small
+per-tile compression output, section "What was tried and not shipped").
+The sparsity-0 case equals plain scaled-dot-product attention (FastH3 4-step
+Preview, same section, the self-test against SDPA).
+
+Readings taken where the pages are silent (each one is also listed in the
+design notes of the repository):
+  R1 pooling is the arithmetic mean over a tile's valid tokens;
+  R2 the fine-branch scale is 1/sqrt(D) (the SDPA default); the coarse
+     softmax uses the same scale; top-k works on the unscaled scores;
+  R3 the coarse softmax runs over every key tile, prefix and video, each
+     weighted once;
+  R4 every query tile, prefix included, receives the gated coarse term;
+  R5 out = o_fine + gate * c_tile, with gate shaped like q: [L, H, D];
+  R6 topk is evaluated in IEEE double exactly as written; with no video
+     tiles there is nothing to select (topk 0);
+  R7 ties in the top-k go to the lower tile index; -0 equals +0;
+  R8 fp32 order of pool and scores is fixed so that the integer selection
+     is reproducible: element -> fp32 exactly; pool = sequential fp32 sum over
+     a tile's slots in slot order, then one correctly rounded division by the
+     count; score = sequential fp32 sum over d of separately rounded
+     products (no fused multiply-add), starting from +0;
+  R9 slot order inside a video tile is the (t, y, x) raster of its valid
+     positions, compacted; inside a prefix tile it is packed order;
+  R10 tile order: prefix tiles first in packed order, then video tiles in
+     (t/4, y/4, x/4) raster order;
+  R11 partial tiles hold only their valid tokens: pad keys are masked, pad
+     query rows produce no output, pooling divides by the valid count;
+  R12 prefix tiles hold 64 tokens (the video tile volume); each maximal run
+     of one tag is one segment;
+  R13 all non-video tokens precede all video tokens; video positions are
+     zero-based and cover the grid exactly once.
+
+Pins (tests/test_oracle_pins.py) -- each function is checked against
+something other than itself:
+  topk_count         closed-form values and the double-evaluation case
+  geometry           per-dimension closed-form tile counts on odd grids;
+                     permutation of the packed video order
+  pool_canonical     constant tiles (exact), float64 mean within rounding
+  scores_canonical   float64 dot product within the fp32 error bound;
+                     constructed exact cases
+  select_topk        exhaustive Python sort on (-score, index); forced ties
+  fine / fine_item   sparsity 0 == torch SDPA (float64) on the packed
+                     sequence; prefix rows == dense rows at any sparsity;
+                     token-level masked dense attention on tiny grids
+  coarse             closed form on tile-constant inputs (== dense attention);
+                     all-equal pooled keys -> mean of pooled values
+  combine            gate 0 -> out == o; tile-constant inputs, gate 1 ->
+                     out == 2 * dense; per-channel gates
+No function here is marked "parity unpinned"; the numeric values of a real
+FastH3 forward are not printed anywhere on the pages, so parity rests on the
+pins above.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+TEXT, COND, AUDIO, VIDEO = 0, 1, 2, 3
+TILE_TOKENS = 64
+TILE_DIMS = (4, 4, 4)
+
+
+class GeometryError(ValueError):
+    pass
+
+
+@dataclass
+class Geometry:
+    L: int
+    P: int                  # prefix tiles
+    NV: int                 # video tiles
+    tiles: list             # per tile: int64 array of packed indices in slot order
+    tile_tag: np.ndarray    # [Nt] segment tag of each tile
+    grid: tuple
+
+    @property
+    def Nt(self) -> int:
+        return self.P + self.NV
+
+    @property
+    def valid(self) -> np.ndarray:
+        return np.array([len(t) for t in self.tiles], dtype=np.int64)
+
+    def tile_of_token(self) -> np.ndarray:
+        out = np.full(self.L, -1, dtype=np.int64)
+        for j, idx in enumerate(self.tiles):
+            out[idx] = j
+        return out
+
+    def slot_of_token(self) -> np.ndarray:
+        out = np.full(self.L, -1, dtype=np.int64)
+        for idx in self.tiles:
+            out[idx] = np.arange(len(idx))
+        return out
+
+    def perm(self) -> np.ndarray:
+        """[Nt, 64] packed index of each slot, -1 for pad slots."""
+        p = np.full((self.Nt, TILE_TOKENS), -1, dtype=np.int64)
+        for j, idx in enumerate(self.tiles):
+            p[j, :len(idx)] = idx
+        return p
+
+
+def topk_count(n_video_tiles: int, sparsity: float) -> int:
+    """The VSA-H3 top-k rule (FastH3 4-step Preview, "Video Sparse Attention is
+    not optional here"), in IEEE double as written (reading R6)."""
+    if n_video_tiles <= 0:
+        return 0
+    s = float(sparsity)
+    return max(1, min(math.ceil((1.0 - s) * n_video_tiles), n_video_tiles))
+
+
+def geometry(token_tags, position_ids, grid, tile=TILE_DIMS) -> Geometry:
+    """Tile geometry from tags and positions (readings R9-R13)."""
+    if tuple(tile) != TILE_DIMS:
+        raise GeometryError("only (4, 4, 4) video tiles are defined")
+    tags = np.asarray(token_tags, dtype=np.int64).reshape(-1)
+    pos = np.asarray(position_ids, dtype=np.int64).reshape(-1, 3)
+    L = tags.shape[0]
+    if pos.shape[0] != L:
+        raise GeometryError("position_ids length differs from token_tags")
+    if np.any((tags < 0) | (tags > 3)):
+        raise GeometryError("unknown segment tag")
+    is_video = tags == VIDEO
+    nvid = int(is_video.sum())
+    n_pre = L - nvid
+    if np.any(is_video[:n_pre]):
+        raise GeometryError("video tokens must follow every prefix token")
+    T, H, W = (int(g) for g in grid)
+    if min(T, H, W) < 0 or T * H * W != nvid:
+        raise GeometryError("video token count does not match the grid")
+
+    tiles, tile_tag = [], []
+    # Prefix: maximal runs of one tag, cut into 64-token chunks in packed order.
+    start = 0
+    while start < n_pre:
+        end = start
+        while end < n_pre and tags[end] == tags[start]:
+            end += 1
+        for c in range(start, end, TILE_TOKENS):
+            tiles.append(np.arange(c, min(c + TILE_TOKENS, end), dtype=np.int64))
+            tile_tag.append(int(tags[start]))
+        start = end
+    P = len(tiles)
+
+    NV = 0
+    if nvid:
+        vidx = np.nonzero(is_video)[0]
+        vp = pos[vidx]
+        t, y, x = vp[:, 0], vp[:, 1], vp[:, 2]
+        if np.any((t < 0) | (t >= T) | (y < 0) | (y >= H) | (x < 0) | (x >= W)):
+            raise GeometryError("video position outside the grid")
+        cell = (t * H + y) * W + x
+        if np.unique(cell).shape[0] != nvid:
+            raise GeometryError("duplicate video position")
+        nt, nh, nw = -(-T // 4), -(-H // 4), -(-W // 4)
+        NV = nt * nh * nw
+        vtile = ((t // 4) * nh + (y // 4)) * nw + (x // 4)
+        # order: by video tile, then (t, y, x) raster inside it
+        order = np.lexsort((x, y, t, vtile))
+        sorted_tile = vtile[order]
+        bounds = np.searchsorted(sorted_tile, np.arange(NV + 1))
+        for j in range(NV):
+            tiles.append(vidx[order[bounds[j]:bounds[j + 1]]])
+            tile_tag.append(VIDEO)
+    return Geometry(L=L, P=P, NV=NV, tiles=tiles, tile_tag=np.array(tile_tag, np.int64),
+                    grid=(T, H, W))
+
+
+def to_f32(x) -> np.ndarray:
+    """Exact conversion of an input tensor (bf16 or fp32, torch or numpy) to fp32."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu").to(torch.float32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(x)
+    if a.dtype != np.float32:
+        raise TypeError("expected fp32 values")
+    return a
+
+
+def pool_canonical(x32: np.ndarray, geom: Geometry) -> np.ndarray:
+    """Per-tile mean of one head's rows, [L, D] fp32 -> [Nt, D] fp32 (R1, R8).
+
+    acc starts at +0 and adds the tile's rows one by one in slot order, each
+    addition rounded to fp32; the mean is one correctly rounded fp32 division.
+    """
+    D = x32.shape[1]
+    perm = geom.perm()
+    n = geom.valid
+    acc = np.zeros((geom.Nt, D), dtype=np.float32)
+    for s in range(TILE_TOKENS):
+        live = np.nonzero(s < n)[0]
+        if live.size == 0:
+            break
+        acc[live] = np.add(acc[live], x32[perm[live, s]], dtype=np.float32)
+    return np.divide(acc, n.astype(np.float32)[:, None], dtype=np.float32)
+
+
+def scores_canonical(qp: np.ndarray, kp: np.ndarray) -> np.ndarray:
+    """S[i, j] = sum_d qp[i, d] * kp[j, d] in the fixed fp32 order of R8."""
+    nq, D = qp.shape
+    S = np.zeros((nq, kp.shape[0]), dtype=np.float32)
+    prod = np.empty_like(S)
+    for d in range(D):
+        np.multiply.outer(qp[:, d], kp[:, d], out=prod)
+        np.add(S, prod, out=S)
+    return S
+
+
+def select_topk(S: np.ndarray, geom: Geometry, topk: int) -> np.ndarray:
+    """Top-k video key tiles of each video query tile (R7), ascending.
+
+    Returns int32 [NV, topk] of global tile indices (P..Nt-1).
+    """
+    P, NV = geom.P, geom.NV
+    if NV == 0:
+        return np.zeros((0, topk), dtype=np.int32)
+    rows = S[P:, P:]
+    order = np.argsort(-rows, axis=1, kind="stable")[:, :topk]
+    return (np.sort(order, axis=1) + P).astype(np.int32)
+
+
+def key_tiles(geom: Geometry, sel: np.ndarray, i: int) -> np.ndarray:
+    """Key tiles visited by query tile i: all tiles for a prefix query tile,
+    prefix tiles plus the selected video tiles for a video query tile."""
+    if i < geom.P:
+        return np.arange(geom.Nt)
+    return np.concatenate([np.arange(geom.P), sel[i - geom.P].astype(np.int64)])
+
+
+def fine_item(q64: np.ndarray, k64: np.ndarray, v64: np.ndarray, geom: Geometry,
+              sel: np.ndarray, i: int, scale: float) -> np.ndarray:
+    """Softmax attention of query tile i's valid rows over the valid tokens of
+    its key tiles (float64, one head).  Returns [n_i, D]."""
+    rows = geom.tiles[i]
+    keys = np.concatenate([geom.tiles[j] for j in key_tiles(geom, sel, i)])
+    logits = (q64[rows] @ k64[keys].T) * scale
+    logits -= logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ v64[keys]
+
+
+def fine(q64, k64, v64, geom: Geometry, sel: np.ndarray, scale: float,
+         items=None) -> np.ndarray:
+    """Fine branch of one head for all query tiles (or ``items``): [L, D] float64,
+    rows of tiles not computed are NaN."""
+    out = np.full((geom.L, q64.shape[1]), np.nan)
+    for i in (range(geom.Nt) if items is None else items):
+        out[geom.tiles[i]] = fine_item(q64, k64, v64, geom, sel, i, scale)
+    return out
+
+
+def coarse(S: np.ndarray, vp: np.ndarray, scale: float) -> np.ndarray:
+    """c[i] = sum_j softmax_j(S[i, j] * scale) * vp[j] over all key tiles (R2, R3),
+    float64.  Returns [Nt, D]."""
+    C = S.astype(np.float64) * scale
+    C -= C.max(axis=1, keepdims=True)
+    p = np.exp(C)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ vp.astype(np.float64)
+
+
+def combine(o: np.ndarray, g: np.ndarray, c: np.ndarray, geom: Geometry) -> np.ndarray:
+    """out[r] = o[r] + gate[r] * c[tile(r)] (R4, R5), float64, one head."""
+    tile = geom.tile_of_token()
+    return o + g.astype(np.float64) * c[tile]
+
+
+def round_bf16_from_f64(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as
+    float64.  One rounding step, straight from float64."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        _, e = np.frexp(x)
+        e = np.maximum(e, -125)                 # below 2^-126: fixed 2^-133 quantum
+        q = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+        big = (2.0 - 2.0 ** -7) * 2.0 ** 127
+        q = np.where(np.abs(q) > big, np.copysign(np.inf, x), q)
+    return np.where(np.isfinite(x), q, x)
+
+
+@dataclass
+class HeadResult:
+    qp: np.ndarray
+    kp: np.ndarray
+    vp: np.ndarray
+    S: np.ndarray
+    sel: np.ndarray
+    c: np.ndarray
+    o: np.ndarray | None        # [L, D] float64 (NaN rows where not computed)
+    out: np.ndarray | None      # [L, D] float64 before I/O rounding
+
+
+def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
+                 with_fine: bool = True) -> HeadResult:
+    """The whole forward for head h.  q, k, v, gate: [L, H, D] (torch or numpy)."""
+    qh = to_f32(q[:, h, :])
+    kh = to_f32(k[:, h, :])
+    vh = to_f32(v[:, h, :])
+    D = qh.shape[1]
+    scale = 1.0 / math.sqrt(D)
+    qp = pool_canonical(qh, geom)
+    kp = pool_canonical(kh, geom)
+    vp = pool_canonical(vh, geom)
+    S = scores_canonical(qp, kp)
+    sel = select_topk(S, geom, topk)
+    c = coarse(S, vp, scale)
+    o = out = None
+    if with_fine:
+        o = fine(qh.astype(np.float64), kh.astype(np.float64), vh.astype(np.float64),
+                 geom, sel, scale, items)
+        out = combine(o, to_f32(gate[:, h, :]), c, geom)
+    return HeadResult(qp, kp, vp, S, sel, c, o, out)
+
+
+def forward(q, k, v, gate, token_tags, position_ids, grid, sparsity, tile=TILE_DIMS,
+            heads=None):
+    """Whole VSA-H3 forward on all (or the listed) heads.
+
+    Returns a dict with
+      out   [L, H, D] float64, already rounded to the I/O dtype's values
+            (bf16 or fp32 inputs decide), NaN for heads not computed;
+      o, c, qp, kp, vp, S, sel per head (lists indexed by head);
+      geom, topk.
+    """
+    geom = geometry(token_tags, position_ids, grid, tile)
+    topk = topk_count(geom.NV, sparsity)
+    L, H, D = q.shape
+    hs = range(H) if heads is None else heads
+    is_bf16 = str(getattr(q, "dtype", "")).endswith("bfloat16")
+    out = np.full((L, H, D), np.nan)
+    res = {"geom": geom, "topk": topk, "heads": {}}
+    for h in hs:
+        r = forward_head(q, k, v, gate, geom, topk, h)
+        out[:, h, :] = (round_bf16_from_f64(r.out) if is_bf16
+                        else r.out.astype(np.float32).astype(np.float64))
+        res["heads"][h] = r
+    res["out"] = out
+    return res
