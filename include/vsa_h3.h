@@ -1,0 +1,167 @@
+/*
+ * vsa_h3.h -- C ABI of the VSA-H3 attention forward for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (FastH3 4-step Preview (VSA, data-free), section "Video
+ * Sparse Attention is not optional here"): packed tokens [text | cond |
+ * audio | video] are cut into 64-token tiles -- segment-pure prefix tiles
+ * and (4,4,4) tiles over the post-patchify video grid -- derived from token
+ * tags and positions.  Per head, mean-pooled q and k give fp32 tile scores;
+ * every video query tile keeps the top-k video key tiles,
+ *     topk = max(1, min(ceil((1 - sparsity) * n_video_tiles), n_video_tiles)),
+ * plus every prefix key tile; prefix query tiles attend to all tiles.  The
+ * fine branch is block-sparse softmax attention over the kept tiles (FastH3
+ * NVFP4 on RTX PRO 6000, "Block-sparse FP4 attention for VSA tiles").  A
+ * compression branch softmax(scores) @ pool(v) is broadcast over each query
+ * tile's rows, multiplied by a per-token gate with no activation, and added.
+ * The output returns to packed order ("Model integration" on the same page).
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns a vsa_status; on failure vsa_h3_last_error() holds a
+ *     message (thread-local, valid until the next call on the same thread).
+ *     There is no fallback route: an unsupported request is an error.
+ *   - Device buffers are caller-owned.  The library never allocates or frees
+ *     device memory; intermediates live in a caller-provided workspace whose
+ *     size vsa_h3_plan_info() reports.
+ *   - Device work is only enqueued on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream).  Calls do not synchronize, except that
+ *     vsa_h3_plan_upload copies from pageable host memory.
+ *   - Tensors are contiguous, sequence-major [L][heads][head_dim] (batch 1).
+ *   - Indices are int32 on the device (L < 2^31); byte offsets are 64-bit.
+ */
+#ifndef VSA_H3_H
+#define VSA_H3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_E_ARG = -1,          /* bad argument: NULL pointer, size, sparsity outside [0,1] */
+  VSA_E_LAYOUT = -2,       /* token tags: unknown tag, or a video token before a prefix token */
+  VSA_E_POSITIONS = -3,    /* video positions outside the grid, duplicated, or not covering it */
+  VSA_E_UNSUPPORTED = -4,  /* head_dim, tile shape or size outside what the kernels implement */
+  VSA_E_WORKSPACE = -5,    /* workspace NULL, misaligned or smaller than vsa_h3_info.workspace_bytes */
+  VSA_E_HIP = -6           /* a HIP runtime call or kernel launch failed */
+} vsa_status;
+
+typedef enum { VSA_BF16 = 0, VSA_F32 = 1 } vsa_dtype;
+
+/* Segment tags of the packed stream (int64 on the wire). */
+enum { VSA_TAG_TEXT = 0, VSA_TAG_COND = 1, VSA_TAG_AUDIO = 2, VSA_TAG_VIDEO = 3 };
+
+typedef struct { int32_t t, h, w; } vsa_dims3;
+
+typedef struct vsa_h3_plan vsa_h3_plan;   /* opaque; host memory owned by the library */
+
+typedef struct {
+  int64_t L;                 /* tokens */
+  int64_t num_prefix_tiles;  /* P: prefix tiles, ids 0..P-1 */
+  int64_t num_video_tiles;   /* NV: video tiles, ids P..P+NV-1 */
+  int64_t num_tiles;         /* Nt = P + NV */
+  int64_t topk;              /* video key tiles kept per video query tile (0 if NV == 0) */
+  int32_t heads, head_dim;
+  uint64_t workspace_bytes;  /* bytes the workspace must hold */
+} vsa_h3_info;
+
+/* Byte offsets of the intermediates inside the workspace (each 256-aligned).
+ * They are documented so that tests and tools can read intermediates back;
+ * their contents are only meaningful after a forward on the same stream. */
+typedef struct {
+  uint64_t perm;    /* int32 [Nt][64]: packed row of each tile slot, -1 for pad slots */
+  uint64_t valid;   /* int32 [Nt]: valid tokens per tile */
+  uint64_t kt;      /* bf16 [H][Nt][64][D]: keys in tile order, pad rows zero */
+  uint64_t vt;      /* bf16 [H][Nt][D][64]: values in tile order, transposed, pad columns zero */
+  uint64_t qp;      /* fp32 [H][Nt][D]: pooled (mean) q per tile */
+  uint64_t kp;      /* fp32 [H][Nt][D]: pooled k */
+  uint64_t vp;      /* fp32 [H][Nt][D]: pooled v */
+  uint64_t scores;  /* fp32 [H][Nt][Ns]: tile scores, Ns = Nt rounded up to 4; after the
+                       forward each row holds softmax(scores / sqrt(D)) instead */
+  uint64_t coarse;  /* fp32 [H][Nt][D]: compression output per query tile */
+  uint64_t sel;     /* int32 [H][NV][topk]: selected video key tiles, ascending */
+  uint64_t total;   /* == vsa_h3_info.workspace_bytes */
+  int64_t scores_row_stride;  /* Ns */
+} vsa_h3_ws_layout;
+
+/* Top-k rule of VSA-H3 evaluated in IEEE double as written; 0 when
+ * num_video_tiles <= 0; -1 if sparsity is outside [0, 1] or NaN. */
+int64_t vsa_h3_topk(int64_t num_video_tiles, double sparsity);
+
+/* Build the tile geometry (host only; touches no GPU).
+ *   token_tags    host int64 [L], values VSA_TAG_*; every non-video token must
+ *                 precede every video token.  Each maximal run of one prefix
+ *                 tag is a segment, cut into 64-token tiles in packed order
+ *                 (the last tile of a segment may be partial).
+ *   position_ids  host int64 [L][3] (t, y, x), zero-based; read for video
+ *                 tokens only, which must cover grid exactly once.
+ *   grid          post-patchify video grid (T, H, W); T*H*W must equal the
+ *                 number of video tokens.
+ *   tile          must be (4,4,4).
+ *   heads >= 1; head_dim 64 or 128; sparsity in [0, 1].
+ * Video tile of (t,y,x): P + ((t/4)*ceil(H/4) + y/4)*ceil(W/4) + x/4; slot
+ * order inside a tile is the (t,y,x) raster of its valid cells.  Edge tiles
+ * may be partial.  On success *plan_out owns host memory until
+ * vsa_h3_plan_destroy. */
+vsa_status vsa_h3_plan_create(const int64_t* token_tags, const int64_t* position_ids,
+                              int64_t L, vsa_dims3 grid, vsa_dims3 tile, int32_t heads,
+                              int32_t head_dim, double sparsity, vsa_h3_plan** plan_out);
+
+vsa_status vsa_h3_plan_info(const vsa_h3_plan* plan, vsa_h3_info* out);
+vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out);
+
+/* Host copies of the plan tables into caller-provided host buffers (any may
+ * be NULL): perm int32 [Nt*64], valid int32 [Nt], tile_slot int32 [L] (tile*64
+ * + slot of each packed token). */
+vsa_status vsa_h3_plan_tables(const vsa_h3_plan* plan, int32_t* perm, int32_t* valid,
+                              int32_t* tile_slot);
+
+/* Copy the plan's tables into the workspace (device).  Must precede the first
+ * vsa_h3_forward with this plan and workspace; they stay valid while the
+ * caller does not overwrite that region. */
+vsa_status vsa_h3_plan_upload(const vsa_h3_plan* plan, void* workspace,
+                              uint64_t workspace_bytes, void* stream);
+
+/* Enqueue the whole forward.
+ *   q, k, v, gate  device [L][heads][head_dim] of io_dtype, read only.
+ *   out            device [L][heads][head_dim] of io_dtype, fully written.
+ *                  out = o_fine + gate * c[tile of the token], rounded to
+ *                  io_dtype (nearest even).  Must not alias the inputs.
+ *   sel_idx        device int32 [heads][NV][topk] or NULL; receives the
+ *                  selected video key tiles (global tile ids, ascending).
+ *                  NULL keeps them in the workspace only.
+ *   workspace      device, 256-byte aligned, >= workspace_bytes, holding the
+ *                  tables from vsa_h3_plan_upload.  Calls that overlap in
+ *                  time must use different workspaces.
+ * Errors: VSA_E_ARG for NULL buffers or an unknown dtype, VSA_E_WORKSPACE,
+ * VSA_E_HIP if a launch fails (execution errors surface on the stream). */
+vsa_status vsa_h3_forward(const vsa_h3_plan* plan, const void* q, const void* k, const void* v,
+                          const void* gate, vsa_dtype io_dtype, void* out, int32_t* sel_idx,
+                          void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* One-call form: builds (or reuses from an internal, thread-safe cache) the
+ * plan for these tags / positions / grid / sizes, uploads its tables into the
+ * workspace and runs vsa_h3_forward.  Query the workspace size first with
+ * vsa_h3_oneshot_workspace_bytes (same arguments). */
+vsa_status vsa_h3_oneshot_workspace_bytes(const int64_t* token_tags, const int64_t* position_ids,
+                                          int64_t L, vsa_dims3 grid, vsa_dims3 tile,
+                                          int32_t heads, int32_t head_dim, double sparsity,
+                                          uint64_t* bytes_out);
+vsa_status vsa_h3_forward_oneshot(const void* q, const void* k, const void* v, const void* gate,
+                                  const int64_t* token_tags, const int64_t* position_ids,
+                                  int64_t L, int32_t heads, int32_t head_dim, vsa_dims3 grid,
+                                  double sparsity, vsa_dims3 tile, vsa_dtype io_dtype, void* out,
+                                  int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
+                                  void* stream);
+
+void vsa_h3_plan_destroy(vsa_h3_plan* plan);
+const char* vsa_h3_last_error(void);
+const char* vsa_h3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSA_H3_H */

@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests (imported by tests only)."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import video_dit_block_amd as vsa
+
+# Acceptance bar for the floating-point output (bf16 I/O, fp32 accumulation):
+# max-abs 2e-2 and relative L2 5e-3 against the oracle.  Coarse intermediates
+# are fp32 on both sides; the pooled q/k/v and the selection are bit-exact.
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    import pytest
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def to_dev(x, dev="cuda"):
+    return {k: (v.to(dev) if k in ("q", "k", "v", "gate") else v) for k, v in x.items()}
+
+
+def run(x, grid, sparsity, dev="cuda", plan=None):
+    """GPU forward through the C ABI.  Returns (out, sel, plan, workspace)."""
+    xd = {k: x[k].to(dev) for k in ("q", "k", "v", "gate")}
+    L, H, D = xd["q"].shape
+    if plan is None:
+        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity)
+    out, sel = vsa.forward(xd["q"], xd["k"], xd["v"], xd["gate"], plan=plan, return_sel=True)
+    torch.cuda.synchronize()
+    ws = plan.workspace(xd["q"].device)
+    return out, sel, plan, ws
+
+
+def intermediates(plan, ws):
+    H, D, Nt = plan.heads, plan.head_dim, plan.num_tiles
+    ns = plan.layout.scores_row_stride
+    return {
+        "qp": plan.view(ws, "qp", torch.float32, (H, Nt, D)).cpu().numpy(),
+        "kp": plan.view(ws, "kp", torch.float32, (H, Nt, D)).cpu().numpy(),
+        "vp": plan.view(ws, "vp", torch.float32, (H, Nt, D)).cpu().numpy(),
+        "coarse": plan.view(ws, "coarse", torch.float32, (H, Nt, D)).cpu().numpy(),
+        "kt": plan.view(ws, "kt", torch.int16, (H, Nt, 64, D)).cpu(),
+        "vt": plan.view(ws, "vt", torch.int16, (H, Nt, D, 64)).cpu(),
+        "probs": plan.view(ws, "scores", torch.float32, (H, Nt, ns)).cpu().numpy()[:, :, :Nt],
+    }
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d) / den) if den > 0 else float(np.linalg.norm(d))
+    return max_abs, rel
+
+
+def assert_close(got, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2):
+    ma, rl = errors(got, ref)
+    say(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e}")
+    assert ma <= max_abs and rl <= rel_l2, (what, ma, rl)
+
+
+def out_f64(out: torch.Tensor) -> np.ndarray:
+    return out.detach().to("cpu").to(torch.float64).numpy()

@@ -1,0 +1,208 @@
+"""GPU parity of the VSA-H3 forward (through the C ABI) against the CPU oracle.
+
+Bar: selected tile sets and pooled q/k/v bit-exact; the output within max-abs
+2e-2 and relative L2 5e-3 (bf16 I/O, fp32 accumulation).  Small layouts are
+compared element by element on every row; the full-size 768p layouts run in
+the same launch configuration as the benchmark and are compared on sampled
+heads and query tiles that the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import video_dit_block_amd as vsa
+from tests.gpu_helpers import (assert_close, errors, intermediates, out_f64, require_gpu, run,
+                               say)
+from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
+    return x.to(torch.bfloat16).view(torch.int16)
+
+
+def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True):
+    """Run the GPU forward and compare everything with the oracle on `heads`."""
+    out, sel, plan, ws = run(x, w.grid, sparsity)
+    H = w.heads
+    heads = list(range(H)) if heads is None else heads
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
+    topk = oracle.topk_count(g.NV, sparsity)
+    assert plan.topk == topk and tuple(sel.shape) == (H, g.NV, topk)
+    inter = intermediates(plan, ws)
+    sel_h = sel.cpu().numpy()
+    got = out_f64(out)
+    is_bf16 = w.io_dtype == "bf16"
+    for h in heads:
+        r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, h)
+        assert np.array_equal(inter["qp"][h], r.qp), f"pooled q head {h}"
+        assert np.array_equal(inter["kp"][h], r.kp), f"pooled k head {h}"
+        assert np.array_equal(inter["vp"][h], r.vp), f"pooled v head {h}"
+        assert np.array_equal(sel_h[h], r.sel), f"selection head {h}"
+        ma, rl = errors(inter["coarse"][h], r.c)
+        assert ma < 1e-5 * max(1.0, float(np.abs(r.c).max())) + 1e-6, ("coarse", h, ma)
+        ref = oracle.round_bf16_from_f64(r.out) if is_bf16 else r.out.astype(np.float32)
+        assert_close(got[:, h, :], ref, f"out head {h}")
+        if check_tiles:
+            perm = g.perm()
+            kt_ref = torch.zeros((g.Nt, 64, w.head_dim), dtype=torch.int16)
+            vt_ref = torch.zeros((g.Nt, 64, w.head_dim), dtype=torch.int16)
+            for j in range(g.Nt):
+                idx = torch.as_tensor(perm[j][perm[j] >= 0])
+                kt_ref[j, :len(idx)] = _bf16_bits(x["k"][idx, h])
+                vt_ref[j, :len(idx)] = _bf16_bits(x["v"][idx, h])
+            assert torch.equal(inter["kt"][h], kt_ref), f"K tiles head {h}"
+            assert torch.equal(inter["vt"][h], vt_ref.transpose(1, 2)), f"V^T tiles head {h}"
+    return out, sel, plan, ws
+
+
+def test_tiny_full_parity():
+    w = WORKLOADS["tiny"]
+    say(f"case tiny: {w.description}")
+    x = make_inputs(w)
+    full_check(w, x, w.sparsity)
+
+
+def test_tiny_sparsity0_equals_dense_sdpa():
+    w = WORKLOADS["tiny"]
+    x = make_inputs(w)
+    x["gate"] = torch.zeros_like(x["gate"])
+    out, sel, plan, _ = run(x, w.grid, 0.0)
+    assert plan.topk == 8
+    q, k, v = (x[n].to(torch.float64).permute(1, 0, 2)[None] for n in ("q", "k", "v"))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[0].permute(1, 0, 2).numpy()
+    assert_close(out_f64(out), ref, "tiny s=0 vs SDPA")
+
+
+LAYOUTS = [
+    # name, heads, D, io, prefix, grid, sparsity, order
+    ("odd_f32_d64_h3", 3, 64, "f32", ((TEXT, 70), (COND, 20), (AUDIO, 33)), (5, 6, 7), 0.5, "shuffled"),
+    ("odd_bf16_d128_h8", 8, 128, "bf16", ((TEXT, 130), (AUDIO, 64)), (9, 10, 11), 0.7, "shuffled"),
+    ("odd_bf16_d64_h16", 16, 64, "bf16", ((COND, 1),), (6, 8, 13), 0.8, "raster"),
+    ("d128_h8_s0", 8, 128, "bf16", ((TEXT, 64),), (8, 8, 12), 0.0, "raster"),
+    ("d128_h8_s1", 8, 128, "bf16", ((TEXT, 64), (AUDIO, 64)), (8, 12, 8), 1.0, "shuffled"),
+    ("video_only_h8", 8, 128, "bf16", (), (8, 8, 16), 0.6, "raster"),
+    ("prefix_only_h2", 2, 128, "bf16", ((TEXT, 100), (AUDIO, 77)), (0, 0, 0), 0.5, "raster"),
+    ("single_tile_h4", 4, 64, "f32", ((TEXT, 5),), (1, 1, 1), 0.5, "raster"),
+]
+
+
+@pytest.mark.parametrize("name,H,D,io,prefix,grid,s,order", LAYOUTS, ids=[l[0] for l in LAYOUTS])
+def test_layouts_full_parity(name, H, D, io, prefix, grid, s, order):
+    w = Workload(name, H, D, io, prefix, grid, s)
+    say(f"case {name}: L={w.L} heads={H} D={D} {io} grid={grid} s={s} {order}")
+    x = make_inputs(w, seed=3, video_order=order)
+    full_check(w, x, s)
+
+
+def test_empty_sequence_is_a_noop():
+    plan = vsa.Plan(np.zeros(0, np.int64), np.zeros((0, 3), np.int64), (0, 0, 0), 2, 64, 0.5)
+    x = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    out = vsa.forward(x, x, x, x, plan=plan)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2, 64)
+
+
+def test_480p5s_full_parity():
+    w = WORKLOADS["480p5s"]
+    say(f"case 480p5s: {w.description}")
+    x = make_inputs(w)
+    out, sel, plan, ws = full_check(w, x, w.sparsity, heads=[0, 1, 7, 8, 30, 55],
+                                    check_tiles=False)
+    # selection of every head against the oracle (pool + scores only)
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
+    sel_h = sel.cpu().numpy()
+    for h in range(w.heads):
+        r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, plan.topk, h,
+                                with_fine=False)
+        assert np.array_equal(sel_h[h], r.sel), h
+
+
+def test_repeatable_and_oneshot_identical():
+    w = WORKLOADS["480p5s"].with_(heads=8)
+    x = make_inputs(w, seed=1)
+    out1, sel1, plan, ws = run(x, w.grid, w.sparsity)
+    out2, sel2, _, _ = run(x, w.grid, w.sparsity, plan=plan)
+    assert torch.equal(out1, out2) and torch.equal(sel1, sel2)
+    xd = {n: x[n].cuda() for n in ("q", "k", "v", "gate")}
+    nbytes = vsa.vsa_h3_oneshot_workspace_bytes(x["token_tags"], x["position_ids"], w.grid,
+                                                (4, 4, 4), 8, 128, w.sparsity)
+    ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out3 = torch.empty_like(xd["q"])
+    sel3 = torch.empty_like(sel1)
+    vsa.vsa_h3_forward_oneshot(xd["q"].data_ptr(), xd["k"].data_ptr(), xd["v"].data_ptr(),
+                               xd["gate"].data_ptr(), x["token_tags"].numpy(),
+                               x["position_ids"].numpy(), 8, 128, w.grid, w.sparsity, (4, 4, 4),
+                               vsa.VSA_BF16, out3.data_ptr(), sel3.data_ptr(), ws2.data_ptr(),
+                               nbytes, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out3) and torch.equal(sel1, sel3)
+
+
+# ----------------------------------------------------------------- full-size 768p layouts
+def _sampled_items(g, sel_rows, rng, n_video=10):
+    items = [0, g.P - 1] if g.P else []
+    partial = [j for j in range(g.P, g.Nt) if g.valid[j] < 64]
+    video = [g.P, g.Nt - 1] + (partial[:1] + partial[-1:] if partial else [])
+    video += list(rng.choice(np.arange(g.P, g.Nt), size=n_video, replace=False))
+    return sorted(set(items + [int(v) for v in video]))
+
+
+def sampled_check(name, heads):
+    w = WORKLOADS[name]
+    say(f"case {name}: {w.description}; oracle heads {heads}")
+    x = make_inputs(w)
+    out, sel, plan, ws = run(x, w.grid, w.sparsity)
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
+    topk = oracle.topk_count(g.NV, w.sparsity)
+    sel_all = sel.cpu().numpy()
+    # properties that hold for every head
+    assert sel_all.shape == (w.heads, g.NV, topk)
+    assert np.all(np.diff(sel_all, axis=2) > 0)
+    assert sel_all.min() >= g.P and sel_all.max() < g.Nt
+    assert torch.isfinite(out).all()
+    inter = intermediates(plan, ws)
+    rng = np.random.default_rng(123)
+    for h in heads:
+        r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, h, with_fine=False)
+        assert np.array_equal(inter["qp"][h], r.qp), h
+        assert np.array_equal(inter["kp"][h], r.kp), h
+        assert np.array_equal(sel_all[h], r.sel), h
+        ma, _ = errors(inter["coarse"][h], r.c)
+        assert ma < 1e-5 * max(1.0, float(np.abs(r.c).max())) + 1e-6, ("coarse", h, ma)
+        items = _sampled_items(g, sel_all[h], rng)
+        q64 = oracle.to_f32(x["q"][:, h, :]).astype(np.float64)
+        k64 = oracle.to_f32(x["k"][:, h, :]).astype(np.float64)
+        v64 = oracle.to_f32(x["v"][:, h, :]).astype(np.float64)
+        gate = oracle.to_f32(x["gate"][:, h, :]).astype(np.float64)
+        scale = 1.0 / math.sqrt(w.head_dim)
+        got_rows, ref_rows = [], []
+        for i in items:
+            o = oracle.fine_item(q64, k64, v64, g, r.sel, i, scale)
+            rows = g.tiles[i]
+            ref = oracle.round_bf16_from_f64(o + gate[rows] * r.c[i])
+            got_rows.append(out[torch.as_tensor(rows), h, :].to(torch.float64).cpu().numpy())
+            ref_rows.append(ref)
+        assert_close(np.concatenate(got_rows), np.concatenate(ref_rows),
+                     f"out head {h} ({len(items)} query tiles)")
+
+
+def test_768p10s_sampled_parity():
+    sampled_check("768p10s", heads=[0, 29, 55])
+
+
+def test_768p10s_smooth_sampled_parity():
+    sampled_check("768p10s_smooth", heads=[3, 44])
+
+
+def test_768p15s_smooth_sampled_parity():
+    sampled_check("768p15s_smooth", heads=[0, 50])

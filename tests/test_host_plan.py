@@ -1,0 +1,203 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and exports
+every function include/vsa_h3.h declares, plan geometry matches the oracle's
+independent geometry, error codes, and workspace layout."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import video_dit_block_amd as vsa
+from video_dit_block_amd import _abi
+from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa_h3.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_h3_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _abi.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_abi.EXPORTED)
+    assert vsa.vsa_h3_version().startswith("vsa_h3")
+
+
+def test_topk_matches_golden_and_oracle():
+    path = os.path.join(ROOT, "tests", "golden", "topk_cases.txt")
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            n, s, k = line.split()[:3]
+            assert vsa.vsa_h3_topk(int(n), float(s)) == int(k)
+    for n in (1, 3, 8, 216, 1260, 1764):
+        for s in np.linspace(0, 1, 41):
+            assert vsa.vsa_h3_topk(n, float(s)) == oracle.topk_count(n, float(s))
+    assert vsa.vsa_h3_topk(0, 0.5) == 0
+    assert vsa.vsa_h3_topk(10, 1.5) == -1
+    assert vsa.vsa_h3_topk(10, float("nan")) == -1
+
+
+LAYOUTS = [
+    ("tiny", WORKLOADS["tiny"], "raster"),
+    ("odd", Workload("odd", 3, 64, "f32", ((TEXT, 70), (COND, 20), (AUDIO, 33)), (5, 6, 7), 0.5), "shuffled"),
+    ("odd2", Workload("odd2", 2, 128, "bf16", ((AUDIO, 1),), (9, 2, 13), 0.3), "shuffled"),
+    ("video_only", Workload("vo", 2, 64, "f32", (), (4, 8, 8), 0.5), "raster"),
+    ("prefix_only", Workload("po", 2, 64, "f32", ((TEXT, 100),), (0, 0, 0), 0.5), "raster"),
+    ("480p5s", WORKLOADS["480p5s"], "raster"),
+    ("768p10s", WORKLOADS["768p10s"], "raster"),
+]
+
+
+@pytest.mark.parametrize("name,w,order", LAYOUTS, ids=[l[0] for l in LAYOUTS])
+def test_plan_geometry_matches_oracle(name, w, order):
+    tags, pos = make_layout(w, order, seed=11)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    g = oracle.geometry(tags.numpy(), pos.numpy(), w.grid)
+    assert (p.num_prefix_tiles, p.num_video_tiles, p.num_tiles) == (g.P, g.NV, g.Nt)
+    assert p.topk == oracle.topk_count(g.NV, w.sparsity)
+    perm, valid, tile_slot = p.tables()
+    assert np.array_equal(valid, g.valid)
+    assert np.array_equal(perm, g.perm())
+    expect_ts = g.tile_of_token() * 64 + g.slot_of_token()
+    assert np.array_equal(tile_slot, expect_ts)
+
+
+def test_plan_sizes_768p10s_and_768p15s():
+    for name, P, NV, topk, n32 in (("768p10s", 16, 1260, 252, 252), ("768p15s_smooth", 48, 1764, 177, 0)):
+        w = WORKLOADS[name]
+        tags, pos = make_layout(w)
+        p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+        assert (p.num_prefix_tiles, p.num_video_tiles, p.topk) == (P, NV, topk)
+        _, valid, _ = p.tables()
+        if name == "768p10s":
+            assert (valid[P:] == 32).sum() == 252 and (valid[P:] == 64).sum() == 1008
+        else:
+            assert (valid[P:] == 48).sum() == 252 and (valid[P:] == 64).sum() == 1512
+
+
+def test_workspace_layout_aligned_disjoint_and_64bit():
+    w = WORKLOADS["768p15s_smooth"]
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    lo = p.layout
+    H, D, Nt, NV, k = w.heads, w.head_dim, p.num_tiles, p.num_video_tiles, p.topk
+    ns = (Nt + 3) // 4 * 4
+    regions = [("perm", Nt * 64 * 4), ("valid", Nt * 4), ("kt", H * Nt * 64 * D * 2),
+               ("vt", H * Nt * 64 * D * 2), ("qp", H * Nt * D * 4), ("kp", H * Nt * D * 4),
+               ("vp", H * Nt * D * 4), ("scores", H * Nt * ns * 4), ("coarse", H * Nt * D * 4),
+               ("sel", H * NV * k * 4)]
+    spans = []
+    for n, size in regions:
+        off = getattr(lo, n)
+        assert off % 256 == 0
+        spans.append((off, off + size))
+    spans.sort()
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert spans[-1][1] <= lo.total == p.workspace_bytes
+    assert lo.scores_row_stride == ns
+    assert lo.total > 2 ** 32          # 64-bit offsets are needed at this size
+
+
+def _raw_create(tags, pos, grid, tile=(4, 4, 4), heads=2, D=64, s=0.5):
+    return _abi.lib().vsa_h3_plan_create(
+        np.ascontiguousarray(tags, np.int64).ctypes.data_as(_abi._I64P),
+        np.ascontiguousarray(pos, np.int64).ctypes.data_as(_abi._I64P),
+        len(tags), _abi.Dims3(*grid), _abi.Dims3(*tile), heads, D, s, ctypes.byref(ctypes.c_void_p()))
+
+
+@pytest.mark.parametrize("case,status", [
+    ("ok", 0), ("video_first", -2), ("badtag", -2), ("dup", -3), ("outside", -3),
+    ("count", -3), ("sparsity", -1), ("sparsity_nan", -1), ("heads", -1), ("head_dim", -4),
+    ("tile", -4), ("neg_grid", -1)])
+def test_plan_error_codes(case, status):
+    w = Workload("e", 2, 64, "f32", ((TEXT, 10),), (4, 4, 4), 0.5)
+    tags, pos = make_layout(w)
+    tags, pos = tags.numpy().copy(), pos.numpy().copy()
+    kw = {}
+    grid = w.grid
+    if case == "video_first":
+        tags[[0, 20]] = tags[[20, 0]]
+    elif case == "badtag":
+        tags[2] = 7
+    elif case == "dup":
+        pos[20] = pos[21]
+    elif case == "outside":
+        pos[20, 1] = -1
+    elif case == "count":
+        grid = (4, 4, 5)
+    elif case == "sparsity":
+        kw["s"] = 1.5
+    elif case == "sparsity_nan":
+        kw["s"] = float("nan")
+    elif case == "heads":
+        kw["heads"] = 0
+    elif case == "head_dim":
+        kw["D"] = 96
+    elif case == "tile":
+        kw["tile"] = (2, 2, 2)
+    elif case == "neg_grid":
+        grid = (-1, 4, 4)
+    st = _raw_create(tags, pos, grid, **kw)
+    assert st == status, _abi.vsa_h3_last_error()
+    if status:
+        assert _abi.vsa_h3_last_error()
+        with pytest.raises(vsa.VsaError):
+            vsa.Plan(tags, pos, grid, kw.get("heads", 2), kw.get("D", 64), kw.get("s", 0.5),
+                     kw.get("tile", (4, 4, 4)))
+
+
+def test_forward_argument_errors_before_any_device_work():
+    w = WORKLOADS["tiny"]
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    L = _abi.lib()
+    fake = 1 << 40  # never dereferenced: every call below fails its checks first
+    assert L.vsa_h3_forward(p.handle, fake, fake, fake, fake, 0, fake + (1 << 30), None,
+                            None, 0, None) == _abi.VSA_E_WORKSPACE
+    assert L.vsa_h3_forward(p.handle, fake, fake, fake, fake, 0, fake + (1 << 30), None,
+                            fake + 8, p.workspace_bytes, None) == _abi.VSA_E_WORKSPACE
+    assert L.vsa_h3_forward(p.handle, fake, fake, fake, fake, 0, fake + (1 << 30), None,
+                            fake, p.workspace_bytes - 1, None) == _abi.VSA_E_WORKSPACE
+    assert L.vsa_h3_forward(p.handle, fake, fake, fake, fake, 7, fake + (1 << 30), None,
+                            fake, p.workspace_bytes, None) == _abi.VSA_E_ARG
+    assert L.vsa_h3_forward(p.handle, None, fake, fake, fake, 0, fake + (1 << 30), None,
+                            fake, p.workspace_bytes, None) == _abi.VSA_E_ARG
+    # out aliasing an input
+    assert L.vsa_h3_forward(p.handle, fake, fake, fake, fake, 0, fake + 64, None,
+                            fake, p.workspace_bytes, None) == _abi.VSA_E_ARG
+    assert L.vsa_h3_forward(None, fake, fake, fake, fake, 0, fake, None, fake, 1,
+                            None) == _abi.VSA_E_ARG
+
+
+def test_oneshot_workspace_bytes_matches_plan():
+    w = WORKLOADS["480p5s"]
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    n = vsa.vsa_h3_oneshot_workspace_bytes(tags.numpy(), pos.numpy(), w.grid, (4, 4, 4), w.heads,
+                                           w.head_dim, w.sparsity)
+    assert n == p.workspace_bytes
+
+
+def test_empty_sequence_plan():
+    p = vsa.Plan(np.zeros(0, np.int64), np.zeros((0, 3), np.int64), (0, 0, 0), 2, 64, 0.5)
+    assert (p.L, p.num_tiles, p.topk) == (0, 0, 0)
+
+
+def test_python_forward_refuses_cpu_tensors():
+    import torch
+    w = WORKLOADS["tiny"]
+    tags, pos = make_layout(w)
+    x = torch.zeros((w.L, w.heads, w.head_dim))
+    with pytest.raises(vsa.VsaError):
+        vsa.forward(x, x, x, x, tags, pos, w.grid, w.sparsity)

@@ -1,0 +1,176 @@
+"""VSA-H3 attention forward on AMD Instinct MI355X (gfx950).
+
+Video Sparse Attention as used by the FastH3 / MiniMax-H3 video DiT: packed
+[text | cond | audio | video] tokens are cut into 64-token tiles, a coarse
+branch scores mean-pooled tiles and produces a gated compression output, each
+video query tile keeps its top-k video key tiles (plus every prefix tile), and
+a block-sparse flash attention computes the fine branch.  All of it runs in
+hand-written HIP kernels behind the C ABI of ``include/vsa_h3.h``; this module
+only marshals arguments (PyTorch provides device memory and the stream).
+
+    import video_dit_block_amd as vsa
+    out = vsa.forward(q, k, v, gate, token_tags, position_ids, grid=(T, H, W),
+                      sparsity=0.8)
+"""
+from __future__ import annotations
+
+import hashlib
+import threading
+from collections import OrderedDict
+
+import numpy as np
+
+from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
+    EXPORTED, LIB_PATH, VSA_BF16, VSA_F32, VSA_TAG_AUDIO, VSA_TAG_COND, VSA_TAG_TEXT,
+    VSA_TAG_VIDEO, VsaError, lib, vsa_h3_forward, vsa_h3_forward_oneshot, vsa_h3_last_error,
+    vsa_h3_oneshot_workspace_bytes, vsa_h3_plan_create, vsa_h3_plan_destroy, vsa_h3_plan_info,
+    vsa_h3_plan_layout, vsa_h3_plan_tables, vsa_h3_plan_upload, vsa_h3_topk, vsa_h3_version,
+)
+
+__all__ = ["Plan", "forward", "VsaError", "vsa_h3_topk", "vsa_h3_version"] + list(EXPORTED)
+
+
+def _host_i64(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu").numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+
+
+class Plan:
+    """Tile geometry for one packed layout (host), plus per-device workspaces."""
+
+    def __init__(self, token_tags, position_ids, grid, heads, head_dim, sparsity,
+                 tile=(4, 4, 4)):
+        self.token_tags = _host_i64(token_tags).reshape(-1)
+        self.position_ids = _host_i64(position_ids).reshape(-1, 3)
+        self.grid = tuple(int(g) for g in grid)
+        self.tile = tuple(int(t) for t in tile)
+        self.sparsity = float(sparsity)
+        self.handle = vsa_h3_plan_create(self.token_tags, self.position_ids, self.grid,
+                                         self.tile, heads, head_dim, sparsity)
+        self.info = vsa_h3_plan_info(self.handle)
+        self.layout = vsa_h3_plan_layout(self.handle)
+        self._ws = {}
+        self._ws_lock = threading.Lock()
+
+    # geometry
+    @property
+    def L(self): return self.info.L
+    @property
+    def heads(self): return self.info.heads
+    @property
+    def head_dim(self): return self.info.head_dim
+    @property
+    def num_prefix_tiles(self): return self.info.num_prefix_tiles
+    @property
+    def num_video_tiles(self): return self.info.num_video_tiles
+    @property
+    def num_tiles(self): return self.info.num_tiles
+    @property
+    def topk(self): return self.info.topk
+    @property
+    def workspace_bytes(self): return self.info.workspace_bytes
+
+    def tables(self):
+        """(perm [Nt, 64], valid [Nt], tile_slot [L]) as host int32 arrays."""
+        return vsa_h3_plan_tables(self.handle)
+
+    def workspace(self, device, stream=None):
+        """The plan's workspace on ``device`` (a torch uint8 tensor), created and
+        filled with the plan's tables on first use."""
+        import torch
+        device = torch.device(device)
+        key = device.index if device.index is not None else torch.cuda.current_device()
+        with self._ws_lock:
+            ws = self._ws.get(key)
+            if ws is None:
+                ws = torch.empty(self.workspace_bytes, dtype=torch.uint8,
+                                 device=torch.device("cuda", key))
+                s = stream if stream is not None else torch.cuda.current_stream(key).cuda_stream
+                vsa_h3_plan_upload(self.handle, ws.data_ptr(), self.workspace_bytes, s)
+                self._ws[key] = ws
+            return ws
+
+    def view(self, ws, name: str, dtype, shape):
+        """A typed view of one workspace region (for tests and tools)."""
+        import torch
+        off = getattr(self.layout, name)
+        n = int(np.prod(shape))
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        return ws[off:off + n * itemsize].view(dtype).view(*shape)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                vsa_h3_plan_destroy(h)
+            except Exception:  # pragma: no cover
+                pass
+            self.handle = None
+
+
+_plans: "OrderedDict[tuple, Plan]" = OrderedDict()
+_plans_lock = threading.Lock()
+
+
+def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4, 4, 4)) -> Plan:
+    """Cached Plan for this exact layout (keyed by a digest of tags and positions)."""
+    tags = _host_i64(token_tags).reshape(-1)
+    pos = _host_i64(position_ids).reshape(-1, 3)
+    digest = hashlib.sha256(tags.tobytes() + b"|" + pos.tobytes()).hexdigest()
+    key = (digest, tuple(grid), tuple(tile), int(heads), int(head_dim), float(sparsity))
+    with _plans_lock:
+        p = _plans.get(key)
+        if p is not None:
+            _plans.move_to_end(key)
+            return p
+    p = Plan(tags, pos, grid, heads, head_dim, sparsity, tile)
+    with _plans_lock:
+        _plans[key] = p
+        while len(_plans) > 8:
+            _plans.popitem(last=False)
+    return p
+
+
+def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsity=None,
+            tile=(4, 4, 4), *, plan: Plan | None = None, out=None, return_sel: bool = False):
+    """VSA-H3 forward.  q, k, v, gate: CUDA tensors [L, heads, head_dim], contiguous,
+    all bfloat16 or all float32.  Returns out (same shape and dtype), and the
+    selected video key tiles int32 [heads, NV, topk] if ``return_sel``."""
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and gate.is_cuda):
+        raise VsaError(-1, "q, k, v and gate must be GPU tensors (there is no CPU path)")
+    if not (q.shape == k.shape == v.shape == gate.shape) or q.dim() != 3:
+        raise VsaError(-1, "q, k, v and gate must share one [L, heads, head_dim] shape")
+    if not (q.dtype == k.dtype == v.dtype == gate.dtype):
+        raise VsaError(-1, "q, k, v and gate must share one dtype")
+    if q.dtype == torch.bfloat16:
+        io = VSA_BF16
+    elif q.dtype == torch.float32:
+        io = VSA_F32
+    else:
+        raise VsaError(-1, f"unsupported dtype {q.dtype}")
+    for t in (q, k, v, gate):
+        if not t.is_contiguous():
+            raise VsaError(-1, "tensors must be contiguous")
+    L, H, D = q.shape
+    if plan is None:
+        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile)
+    if (plan.L, plan.heads, plan.head_dim) != (L, H, D):
+        raise VsaError(-1, "plan does not match the tensors' [L, heads, head_dim]")
+    dev = q.device
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = plan.workspace(dev, stream)
+    if out is None:
+        out = torch.empty_like(q)
+    sel = None
+    if return_sel:
+        sel = torch.empty((H, plan.num_video_tiles, plan.topk), dtype=torch.int32, device=dev)
+    vsa_h3_forward(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), io,
+                   out.data_ptr(), sel.data_ptr() if sel is not None and sel.numel() else None,
+                   ws.data_ptr(), plan.workspace_bytes, stream)
+    return (out, sel) if return_sel else out

@@ -1,0 +1,296 @@
+// Coarse branch and top-k selection of VSA-H3 (FastH3 4-step Preview (VSA,
+// data-free), section "Video Sparse Attention is not optional here"):
+//   S[h][i][j]  = pooled q_i . pooled k_j in fp32           (tile scores)
+//   sel[h][i]   = top-k video key tiles of video query tile i by S
+//   c[h][i][:]  = softmax_j(S[h][i][j] / sqrt(D)) @ pooled v  (compression)
+//
+// Scores are evaluated in a fixed order -- start at +0, add the separately
+// rounded products d = 0..D-1, no fused multiply-add -- so the selection is
+// reproducible bit for bit.  That is why the score contraction runs on the
+// VALU rather than on the matrix cores, whose internal accumulation order is
+// not specified.  The selection breaks ties toward the lower tile index.
+//
+// Three kernels:
+//   scores        64x64 output tile per block, 4x4 per thread, pooled rows
+//                 staged transposed in LDS in chunks of 32 channels;
+//   softmax_topk  one wave per (head, query tile): the row lives in
+//                 registers; an MSB-first bitwise search finds the k-th
+//                 largest key, ties are admitted in ascending index order,
+//                 the kept indices are compacted in ascending order; the row
+//                 is then overwritten with its softmax probabilities;
+//   pv            c = probabilities @ pooled v, 64 rows x D per block.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace vsa {
+
+namespace {
+
+constexpr int kScoreTile = 64;
+constexpr int kDChunk = 32;
+constexpr int kPad = 4;
+
+template <int D>
+__global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qp,
+                                                            const float* __restrict__ kp,
+                                                            int Nt, int Ns,
+                                                            float* __restrict__ S) {
+  __shared__ __attribute__((aligned(16))) float qs[kDChunk][kScoreTile + kPad];
+  __shared__ __attribute__((aligned(16))) float ks[kDChunk][kScoreTile + kPad];
+  const int h = blockIdx.z;
+  const int i0 = blockIdx.y * kScoreTile;
+  const int j0 = blockIdx.x * kScoreTile;
+  const int tid = threadIdx.x;
+  const int ti = tid / 16, tj = tid % 16;
+  const float* qh = qp + static_cast<size_t>(h) * Nt * D;
+  const float* kh = kp + static_cast<size_t>(h) * Nt * D;
+
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+
+  for (int dc = 0; dc < D; dc += kDChunk) {
+    // 64 rows x 32 channels = 512 float4 per operand; 2 per thread.
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int id = tid + e * 256;
+      const int r = id / 8, c4 = id % 8;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (i0 + r < Nt) a = *reinterpret_cast<const float4*>(qh + static_cast<size_t>(i0 + r) * D + dc + 4 * c4);
+      if (j0 + r < Nt) b = *reinterpret_cast<const float4*>(kh + static_cast<size_t>(j0 + r) * D + dc + 4 * c4);
+      qs[4 * c4 + 0][r] = a.x; qs[4 * c4 + 1][r] = a.y; qs[4 * c4 + 2][r] = a.z; qs[4 * c4 + 3][r] = a.w;
+      ks[4 * c4 + 0][r] = b.x; ks[4 * c4 + 1][r] = b.y; ks[4 * c4 + 2][r] = b.z; ks[4 * c4 + 3][r] = b.w;
+    }
+    __syncthreads();
+    {
+#pragma clang fp contract(off)
+#pragma unroll 8
+      for (int dd = 0; dd < kDChunk; ++dd) {
+        const float4 a = *reinterpret_cast<const float4*>(&qs[dd][4 * ti]);
+        const float4 b = *reinterpret_cast<const float4*>(&ks[dd][4 * tj]);
+        const float av[4] = {a.x, a.y, a.z, a.w};
+        const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) acc[x][y] = acc[x][y] + av[x] * bv[y];
+      }
+    }
+    __syncthreads();
+  }
+  const int jc = j0 + 4 * tj;
+  if (jc < Ns) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int i = i0 + 4 * ti + x;
+      if (i < Nt) {
+        *reinterpret_cast<float4*>(S + (static_cast<size_t>(h) * Nt + i) * Ns + jc) =
+            make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+      }
+    }
+  }
+}
+
+// Order-preserving map of fp32 to uint32 (-0 folded onto +0; inputs finite).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int MAXM>
+__global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(float* __restrict__ S, int H,
+                                                                  int Nt, int Ns, int P, int NV,
+                                                                  int topk, float scale_log2,
+                                                                  int32_t* __restrict__ sel) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= H * Nt) return;  // wave-uniform
+  const int h = row / Nt;
+  const int i = row - h * Nt;
+  float* srow = S + static_cast<size_t>(row) * Ns;
+
+  float s[MAXM];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) {
+    const int j = lane + 64 * m;
+    s[m] = j < Nt ? srow[j] : -INFINITY;
+  }
+
+  if (i >= P && topk > 0) {
+    // Keys of the video key tiles j in [P, Nt).
+    uint32_t key[MAXM];
+    bool ok[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      const int j = lane + 64 * m;
+      ok[m] = j >= P && j < Nt;
+      key[m] = ok[m] ? order_key(s[m]) : 0u;
+    }
+    // Largest T with #{key >= T} >= topk, i.e. the topk-th largest key.
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) c += (ok[m] && key[m] >= cand) ? 1 : 0;
+      if (wave_sum_i(c) >= topk) thr = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) gt += (ok[m] && key[m] > thr) ? 1 : 0;
+    const int need = topk - wave_sum_i(gt);  // ties to admit, lowest index first
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    int tie_base = 0, out_base = 0;
+    int32_t* dst = sel + (static_cast<size_t>(h) * NV + (i - P)) * topk;
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      const bool tie = ok[m] && key[m] == thr;
+      const uint64_t tmask = __ballot(tie);
+      const int rank = tie_base + __popcll(tmask & below);
+      tie_base += __popcll(tmask);
+      const bool take = ok[m] && (key[m] > thr || (tie && rank < need));
+      const uint64_t omask = __ballot(take);
+      if (take) dst[out_base + __popcll(omask & below)] = lane + 64 * m;
+      out_base += __popcll(omask);
+    }
+  }
+
+  // Softmax over all key tiles with the 1/sqrt(D) scale (log2 domain).
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) mx = fmaxf(mx, s[m]);
+  mx = wave_max(mx);
+  float e[MAXM];
+  float sum = 0.0f;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) {
+    const int j = lane + 64 * m;
+    e[m] = j < Nt ? __builtin_amdgcn_exp2f((s[m] - mx) * scale_log2) : 0.0f;
+    sum += e[m];
+  }
+  sum = wave_sum(sum);
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) {
+    const int j = lane + 64 * m;
+    if (j < Nt) srow[j] = e[m] * inv;
+  }
+}
+
+// c[h] = Pr[h] @ vp[h]; block = 64 query tiles x D channels, K-loop over 32 key tiles.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict__ Pr,
+                                                        const float* __restrict__ vp, int Nt,
+                                                        int Ns, float* __restrict__ c) {
+  constexpr int CPT = D / 16;   // channels per thread
+  constexpr int KB = 32;
+  __shared__ __attribute__((aligned(16))) float ps[KB][64 + kPad];
+  __shared__ __attribute__((aligned(16))) float vs[KB][D];
+  const int h = blockIdx.y;
+  const int i0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const int tr = tid / 16, tc = tid % 16;
+  const float* ph = Pr + static_cast<size_t>(h) * Nt * Ns;
+  const float* vh = vp + static_cast<size_t>(h) * Nt * D;
+  float acc[4][CPT];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < CPT; ++y) acc[x][y] = 0.0f;
+
+  for (int j0 = 0; j0 < Nt; j0 += KB) {
+    // probabilities: 64 rows x 32 keys = 512 float4, 2 per thread (transposed into LDS)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int id = tid + e * 256;
+      const int r = id / 8, c4 = id % 8;
+      const int j = j0 + 4 * c4;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i0 + r < Nt) {
+        const float* src = ph + static_cast<size_t>(i0 + r) * Ns + j;
+        if (j + 3 < Nt) {
+          a = *reinterpret_cast<const float4*>(src);
+        } else {
+          if (j + 0 < Nt) a.x = src[0];
+          if (j + 1 < Nt) a.y = src[1];
+          if (j + 2 < Nt) a.z = src[2];
+        }
+      }
+      ps[4 * c4 + 0][r] = a.x; ps[4 * c4 + 1][r] = a.y; ps[4 * c4 + 2][r] = a.z; ps[4 * c4 + 3][r] = a.w;
+    }
+    // pooled values: 32 rows x D
+    for (int id = tid; id < KB * D / 4; id += 256) {
+      const int r = id / (D / 4), c4 = id % (D / 4);
+      float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + r < Nt) b = *reinterpret_cast<const float4*>(vh + static_cast<size_t>(j0 + r) * D + 4 * c4);
+      *reinterpret_cast<float4*>(&vs[r][4 * c4]) = b;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < KB; ++jj) {
+      const float4 a = *reinterpret_cast<const float4*>(&ps[jj][4 * tr]);
+      const float av[4] = {a.x, a.y, a.z, a.w};
+      float bv[CPT];
+#pragma unroll
+      for (int y = 0; y < CPT; y += 4) {
+        const float4 b = *reinterpret_cast<const float4*>(&vs[jj][CPT * tc + y]);
+        bv[y] = b.x; bv[y + 1] = b.y; bv[y + 2] = b.z; bv[y + 3] = b.w;
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < CPT; ++y) acc[x][y] = fmaf(av[x], bv[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int i = i0 + 4 * tr + x;
+    if (i < Nt) {
+      float* dst = c + (static_cast<size_t>(h) * Nt + i) * D + CPT * tc;
+#pragma unroll
+      for (int y = 0; y < CPT; y += 4)
+        *reinterpret_cast<float4*>(dst + y) = make_float4(acc[x][y], acc[x][y + 1], acc[x][y + 2], acc[x][y + 3]);
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const CoarseArgs& a, hipStream_t stream) {
+  const int nb = (a.Nt + kScoreTile - 1) / kScoreTile;
+  hipLaunchKernelGGL((coarse_scores_kernel<D>), dim3(nb, nb, a.H), dim3(256), 0, stream, a.qp,
+                     a.kp, a.Nt, a.Ns, a.scores);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  const int rows = a.H * a.Nt;
+  dim3 g2((rows + 3) / 4);
+  const int maxm = (a.Nt + 63) / 64;
+  if (maxm <= 4)
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<4>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+  else if (maxm <= 8)
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<8>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+  else if (maxm <= 16)
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<16>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+  else if (maxm <= 32)
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<32>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+  else
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<64>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  hipLaunchKernelGGL((coarse_pv_kernel<D>), dim3(nb, a.H), dim3(256), 0, stream, a.scores, a.vp,
+                     a.Nt, a.Ns, a.coarse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_coarse(const CoarseArgs& a, hipStream_t stream) {
+  return a.D == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
+}
+
+}  // namespace vsa

@@ -1,0 +1,44 @@
+// Launch interfaces of the gfx950 kernels of the VSA-H3 forward (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa {
+
+struct PermutePoolArgs {
+  const void *q, *k, *v;        // [L][H][D], bf16 or fp32
+  bool io_f32;
+  const int32_t* perm;          // [Nt][64]
+  const int32_t* valid;         // [Nt]
+  int H, Nt, D;
+  uint16_t *kt, *vt;            // [H][Nt][64][D], [H][Nt][D][64] bf16
+  float *qp, *kp, *vp;          // [H][Nt][D]
+};
+hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t stream);
+
+struct CoarseArgs {
+  const float *qp, *kp, *vp;    // [H][Nt][D]
+  float* scores;                // [H][Nt][Ns]
+  float* coarse;                // [H][Nt][D]
+  int32_t* sel;                 // [H][NV][topk]
+  int H, Nt, Ns, P, NV, topk, D;
+};
+hipError_t launch_coarse(const CoarseArgs& a, hipStream_t stream);
+
+struct FineArgs {
+  const void* q;                // [L][H][D] io dtype
+  const void* gate;             // [L][H][D] io dtype
+  void* out;                    // [L][H][D] io dtype
+  bool io_f32;
+  const uint16_t* kt;           // [H][Nt][64][D] bf16
+  const uint16_t* vt;           // [H][Nt][D][64] bf16
+  const float* coarse;          // [H][Nt][D]
+  const int32_t* perm;          // [Nt][64]
+  const int32_t* valid;         // [Nt]
+  const int32_t* sel;           // [H][NV][topk]
+  int H, Nt, P, NV, topk, D;
+};
+hipError_t launch_fine(const FineArgs& a, hipStream_t stream);
+
+}  // namespace vsa

@@ -1,0 +1,186 @@
+// Tile geometry of VSA-H3 (FastH3 4-step Preview (VSA, data-free), section
+// "Video Sparse Attention is not optional here"): segment-pure prefix tiles
+// and (4,4,4) video tiles over the post-patchify grid, derived from the
+// packed stream's tags and positions; the top-k rule of the same passage.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <limits>
+
+namespace vsa {
+
+namespace {
+thread_local std::string g_error;
+
+uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255u); }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+void set_error(const std::string& msg) { g_error = msg; }
+const char* get_error() { return g_error.c_str(); }
+
+int64_t topk_rule(int64_t nv, double s) {
+  if (!(s >= 0.0 && s <= 1.0)) return -1;  // also rejects NaN
+  if (nv <= 0) return 0;
+  // Evaluated in IEEE double exactly as the rule is written.
+  double want = std::ceil((1.0 - s) * static_cast<double>(nv));
+  int64_t k = want >= static_cast<double>(nv) ? nv : static_cast<int64_t>(want);
+  return k < 1 ? 1 : k;
+}
+
+vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_dims3 grid,
+                      vsa_dims3 tile, int32_t heads, int32_t head_dim, double sparsity,
+                      vsa_h3_plan* plan) {
+  if (L < 0 || L >= (int64_t(1) << 31) - kTile) {
+    set_error("L must be in [0, 2^31 - 64)");
+    return VSA_E_ARG;
+  }
+  if (L > 0 && (!tags || !pos)) {
+    set_error("token_tags and position_ids must be non-NULL host arrays");
+    return VSA_E_ARG;
+  }
+  if (heads < 1) {
+    set_error("heads must be >= 1");
+    return VSA_E_ARG;
+  }
+  if (!(sparsity >= 0.0 && sparsity <= 1.0)) {
+    set_error("sparsity must lie in [0, 1]");
+    return VSA_E_ARG;
+  }
+  if (grid.t < 0 || grid.h < 0 || grid.w < 0) {
+    set_error("grid dimensions must be >= 0");
+    return VSA_E_ARG;
+  }
+  if (tile.t != 4 || tile.h != 4 || tile.w != 4) {
+    set_error("only (4,4,4) video tiles are implemented");
+    return VSA_E_UNSUPPORTED;
+  }
+  if (head_dim != 64 && head_dim != 128) {
+    set_error("head_dim must be 64 or 128");
+    return VSA_E_UNSUPPORTED;
+  }
+
+  // Packing: every non-video token precedes every video token.
+  int64_t n_pre = 0;
+  while (n_pre < L && tags[n_pre] != VSA_TAG_VIDEO) {
+    if (tags[n_pre] < 0 || tags[n_pre] > VSA_TAG_VIDEO) {
+      set_error("unknown token tag at index " + std::to_string(n_pre));
+      return VSA_E_LAYOUT;
+    }
+    ++n_pre;
+  }
+  for (int64_t r = n_pre; r < L; ++r) {
+    if (tags[r] != VSA_TAG_VIDEO) {
+      set_error(tags[r] < 0 || tags[r] > VSA_TAG_VIDEO
+                    ? "unknown token tag at index " + std::to_string(r)
+                    : "prefix token after the first video token at index " + std::to_string(r));
+      return VSA_E_LAYOUT;
+    }
+  }
+  const int64_t n_vid = L - n_pre;
+  const int64_t T = grid.t, H = grid.h, W = grid.w;
+  if (T * H * W != n_vid) {
+    set_error("video token count " + std::to_string(n_vid) + " != grid volume " +
+              std::to_string(T * H * W));
+    return VSA_E_POSITIONS;
+  }
+
+  // Prefix tiles: each maximal run of one tag is cut into 64-token chunks.
+  std::vector<int64_t> pre_start, pre_len;
+  for (int64_t s = 0; s < n_pre;) {
+    int64_t e = s;
+    while (e < n_pre && tags[e] == tags[s]) ++e;
+    for (int64_t c = s; c < e; c += kTile) {
+      pre_start.push_back(c);
+      pre_len.push_back(std::min<int64_t>(kTile, e - c));
+    }
+    s = e;
+  }
+  const int64_t P = static_cast<int64_t>(pre_start.size());
+  const int64_t nt = ceil_div(T, 4), nh = ceil_div(H, 4), nw = ceil_div(W, 4);
+  const int64_t NV = n_vid ? nt * nh * nw : 0;
+  const int64_t Nt = P + NV;
+  if (Nt * kTile >= (int64_t(1) << 31)) {
+    set_error("too many tiles for 32-bit slot indices");
+    return VSA_E_UNSUPPORTED;
+  }
+  if (Nt > kMaxTilesCoarse) {
+    set_error("more than " + std::to_string(kMaxTilesCoarse) + " tiles per head is not supported");
+    return VSA_E_UNSUPPORTED;
+  }
+
+  plan->L = L;
+  plan->P = P;
+  plan->NV = NV;
+  plan->Nt = Nt;
+  plan->topk = topk_rule(NV, sparsity);
+  plan->heads = heads;
+  plan->head_dim = head_dim;
+  plan->grid = grid;
+  plan->sparsity = sparsity;
+  plan->perm.assign(static_cast<size_t>(Nt * kTile), -1);
+  plan->valid.assign(static_cast<size_t>(Nt), 0);
+  plan->tile_slot.assign(static_cast<size_t>(L), -1);
+
+  for (int64_t j = 0; j < P; ++j) {
+    plan->valid[j] = static_cast<int32_t>(pre_len[j]);
+    for (int64_t s = 0; s < pre_len[j]; ++s) {
+      plan->perm[j * kTile + s] = static_cast<int32_t>(pre_start[j] + s);
+      plan->tile_slot[pre_start[j] + s] = static_cast<int32_t>(j * kTile + s);
+    }
+  }
+
+  // Video tiles: tile id from the (t/4, y/4, x/4) raster; the slot is the
+  // compact (t, y, x) raster inside the tile's valid extent.
+  std::vector<uint8_t> seen(static_cast<size_t>(n_vid), 0);
+  for (int64_t r = n_pre; r < L; ++r) {
+    const int64_t t = pos[3 * r], y = pos[3 * r + 1], x = pos[3 * r + 2];
+    if (t < 0 || t >= T || y < 0 || y >= H || x < 0 || x >= W) {
+      set_error("video position outside the grid at index " + std::to_string(r));
+      return VSA_E_POSITIONS;
+    }
+    const int64_t cell = (t * H + y) * W + x;
+    if (seen[cell]) {
+      set_error("duplicate video position at index " + std::to_string(r));
+      return VSA_E_POSITIONS;
+    }
+    seen[cell] = 1;
+    const int64_t bt = t / 4, by = y / 4, bx = x / 4;
+    const int64_t et = std::min<int64_t>(4, T - 4 * bt);
+    const int64_t eh = std::min<int64_t>(4, H - 4 * by);
+    const int64_t ew = std::min<int64_t>(4, W - 4 * bx);
+    const int64_t j = P + (bt * nh + by) * nw + bx;
+    const int64_t slot = ((t % 4) * eh + (y % 4)) * ew + (x % 4);
+    plan->valid[j] = static_cast<int32_t>(et * eh * ew);
+    plan->perm[j * kTile + slot] = static_cast<int32_t>(r);
+    plan->tile_slot[r] = static_cast<int32_t>(j * kTile + slot);
+  }
+
+  // Workspace layout; every region 256-byte aligned, sizes in 64-bit.
+  const uint64_t h64 = static_cast<uint64_t>(heads), d64 = static_cast<uint64_t>(head_dim);
+  const uint64_t nt64 = static_cast<uint64_t>(Nt);
+  const int64_t ns = (Nt + 3) / 4 * 4;
+  Layout& lo = plan->layout;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    uint64_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  lo.perm = take(nt64 * kTile * 4);
+  lo.valid = take(nt64 * 4);
+  lo.kt = take(h64 * nt64 * kTile * d64 * 2);
+  lo.vt = take(h64 * nt64 * kTile * d64 * 2);
+  lo.qp = take(h64 * nt64 * d64 * 4);
+  lo.kp = take(h64 * nt64 * d64 * 4);
+  lo.vp = take(h64 * nt64 * d64 * 4);
+  lo.scores = take(h64 * nt64 * static_cast<uint64_t>(ns) * 4);
+  lo.coarse = take(h64 * nt64 * d64 * 4);
+  lo.sel = take(h64 * static_cast<uint64_t>(NV) * static_cast<uint64_t>(plan->topk) * 4);
+  lo.total = off < 256 ? 256 : off;
+  lo.ns = ns;
+  return VSA_OK;
+}
+
+}  // namespace vsa
