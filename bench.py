@@ -1,0 +1,270 @@
+"""Benchmark of the VSA-H3 attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 768p10s]
+
+One step is one whole forward (permute+pool, coarse branch + top-k, fine
+block-sparse attention with the fused gate-combine epilogue) over the
+768p 10-s layout: 73,600 tokens (1,024 prefix + 18x48x84 video), 56 heads,
+head_dim 128, bf16, sparsity 0.8 (topk 252), on seeded synthetic inputs that
+are resident in HBM before the timed region starts.
+
+Prints one JSON line.  ``value`` is the effective throughput in TFLOP/s: the
+algorithmic FLOPs of the selected blocks (valid tokens only, from this run's
+own selection) plus the coarse branch, divided by the measured time per
+forward.  ``roofline`` covers the dominant kernel (fine attention) from HIP
+events recorded on the kernels' stream around each launch; ``cpu_baseline``
+times the CPU oracle on one head of the same workload (a bounded sample) and
+also checks the GPU output of that head against it.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk (MI355X dense bf16 MFMA)
+PEAK_HBM_GBS = 8000.0
+METRIC = "VSA-H3 fwd ms and effective TFLOP/s (% bf16 MFMA peak) at 73.6k tokens"
+FINE_SOURCES = ["video_dit_block_amd/csrc/fine_attn.hip", "video_dit_block_amd/csrc/device.hpp",
+                "video_dit_block_amd/csrc/kernels.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_768p10s_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime (the stage events are recorded
+    by the library on the stream its kernels run on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def fine_flops(sel: np.ndarray, valid: np.ndarray, P: int, L: int, D: int) -> tuple[float, float]:
+    """Algorithmic fine-branch FLOPs (valid tokens only) and the padded-tile
+    FLOPs the MFMA executes, for one forward.  sel: [H, NV, topk] global ids."""
+    H, NV, topk = sel.shape
+    n = valid.astype(np.float64)
+    p_tok = float(n[:P].sum())
+    per_row = p_tok + n[sel].sum(axis=2)                      # [H, NV] keys per video query
+    video = float((per_row * n[P:][None, :]).sum())
+    prefix = float(n[:P].sum()) * L * H
+    alg = 4.0 * D * (video + prefix)
+    pairs = H * (NV * (P + topk) + P * (P + NV))
+    padded = 4.0 * D * 64 * 64 * pairs
+    return alg, padded
+
+
+def sources_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per fine-attention launch from the committed counter summary,
+    or None if it is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256") != sources_digest(FINE_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(x, w, gpu_out, gpu_sel, plan, head=0):
+    """Time the oracle (as it stands) on one head of the workload and check the
+    GPU's output and selection for that head against it."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
+    topk = oracle.topk_count(g.NV, w.sparsity)
+    t0 = time.perf_counter()
+    r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, head)
+    t1 = time.perf_counter()
+    alg, _ = fine_flops(r.sel[None].astype(np.int64), g.valid, g.P, g.L, w.head_dim)
+    flops = alg + 4.0 * w.head_dim * g.Nt ** 2
+    ref = oracle.round_bf16_from_f64(r.out)
+    got = gpu_out[:, head, :].to("cpu").double().numpy()
+    d = got - ref
+    parity = {"head": head, "sel_bit_exact": bool(np.array_equal(gpu_sel[head], r.sel)),
+              "max_abs": float(np.abs(d).max()),
+              "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref))}
+    return {"value": flops / (t1 - t0) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": t1 - t0,
+            "sample": f"head {head} of {w.heads} of the {w.name} workload (whole per-head forward: "
+                      "pool, scores, top-k, coarse, float64 fine branch, combine)"}, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="768p10s")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="counter runs: one 1 GiB device copy (traffic calibration), then the "
+                         "warmup and timed forwards; no CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the forward is single-GPU; multi-GPU sharding is a design note only)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, ROOT)
+    import video_dit_block_amd as vsa
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    log(f"bench: workload {w.name}: {w.description}")
+    t = time.perf_counter()
+    x = make_inputs(w, seed=0)
+    log(f"bench: inputs generated in {time.perf_counter() - t:.1f}s")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    xd = {n: x[n].to(dev) for n in ("q", "k", "v", "gate")}
+    plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim, w.sparsity)
+    stream = torch.cuda.current_stream(dev)
+    ws = plan.workspace(dev, stream.cuda_stream)
+    out = torch.empty_like(xd["q"])
+    sel = torch.empty((w.heads, plan.num_video_tiles, plan.topk), dtype=torch.int32, device=dev)
+    io = vsa.VSA_BF16 if w.io_dtype == "bf16" else vsa.VSA_F32
+    ptrs = [xd[n].data_ptr() for n in ("q", "k", "v", "gate")]
+
+    if args.profile_pass:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                      # calibration copy: 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        del src, dst
+
+    hip = HipEvents()
+    evs = [hip.create(4) for _ in range(args.steps)]
+
+    def step(events=None):
+        vsa.vsa_h3_forward_timed(plan.handle, *ptrs, io, out.data_ptr(), sel.data_ptr(),
+                                 ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream, events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done")
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage = np.array([[hip.elapsed_ms(e[a], e[a + 1]) for a in range(3)] for e in evs])
+    event_ms = np.array([hip.elapsed_ms(e[0], e[3]) for e in evs])
+    for e in evs:
+        hip.destroy(e)
+    log(f"bench: {args.steps} timed steps, {ms_per_step:.3f} ms/step (wall), "
+        f"{event_ms.mean():.3f} ms/step (events)")
+
+    perm, valid, _ = plan.tables()
+    sel_h = sel.cpu().numpy()
+    alg_fine, padded_fine = fine_flops(sel_h.astype(np.int64), valid, plan.num_prefix_tiles,
+                                       plan.L, w.head_dim)
+    coarse_flops = 4.0 * w.head_dim * plan.num_tiles ** 2 * w.heads
+    total = alg_fine + coarse_flops
+    tflops = total / (ms_per_step * 1e-3) / 1e12
+    fine_ms = float(stage[:, 2].mean())
+    fine_tflops = alg_fine / (fine_ms * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "tokens": plan.L, "heads": w.heads, "head_dim": w.head_dim,
+            "prefix_tokens": w.n_prefix_tokens, "grid": list(w.grid),
+            "sparsity": w.sparsity, "topk": plan.topk, "tiles": plan.num_tiles,
+            "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+            "flops_effective": total, "flops_fine_padded_tiles": padded_fine,
+            "stage_ms": {"permute_pool": round(float(stage[:, 0].mean()), 4),
+                         "coarse_topk": round(float(stage[:, 1].mean()), 4),
+                         "fine_attn": round(fine_ms, 4)},
+            "event_ms_per_step": round(float(event_ms.mean()), 4),
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "fine_attn_kernel",
+            "achieved": round(fine_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(fine_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(),
+            "algorithmic_flops_per_launch": alg_fine,
+            "avg_launch_ms": round(fine_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline and not args.profile_pass:
+        log("bench: timing the CPU oracle on one head (bounded sample)")
+        cb, parity = cpu_baseline(x, w, out, sel_h, plan)
+        rec["cpu_baseline"] = cb
+        rec["parity"] = parity
+        log(f"bench: oracle head 0: {cb['seconds']:.1f}s, parity {parity}")
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

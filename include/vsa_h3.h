@@ -142,6 +142,18 @@ vsa_status vsa_h3_forward(const vsa_h3_plan* plan, const void* q, const void* k,
                           const void* gate, vsa_dtype io_dtype, void* out, int32_t* sel_idx,
                           void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* Same as vsa_h3_forward, and records caller-created HIP events (hipEvent_t,
+ * passed as void*) on `stream` at the stage boundaries, for profiling tools:
+ *   events[0] before the permute+pool kernel,
+ *   events[1] after it (before the coarse-branch kernels),
+ *   events[2] after the coarse branch (before the fine attention kernel),
+ *   events[3] after the fine attention kernel.
+ * `events` must point to 4 valid events; NULL behaves like vsa_h3_forward. */
+vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const void* k,
+                                const void* v, const void* gate, vsa_dtype io_dtype, void* out,
+                                int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
+                                void* stream, void* const* events);
+
 /* One-call form: builds (or reuses from an internal, thread-safe cache) the
  * plan for these tags / positions / grid / sizes, uploads its tables into the
  * workspace and runs vsa_h3_forward.  Query the workspace size first with

@@ -22,7 +22,8 @@ import numpy as np
 
 from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
     EXPORTED, LIB_PATH, VSA_BF16, VSA_F32, VSA_TAG_AUDIO, VSA_TAG_COND, VSA_TAG_TEXT,
-    VSA_TAG_VIDEO, VsaError, lib, vsa_h3_forward, vsa_h3_forward_oneshot, vsa_h3_last_error,
+    VSA_TAG_VIDEO, VsaError, lib, vsa_h3_forward, vsa_h3_forward_oneshot, vsa_h3_forward_timed,
+    vsa_h3_last_error,
     vsa_h3_oneshot_workspace_bytes, vsa_h3_plan_create, vsa_h3_plan_destroy, vsa_h3_plan_info,
     vsa_h3_plan_layout, vsa_h3_plan_tables, vsa_h3_plan_upload, vsa_h3_topk, vsa_h3_version,
 )

@@ -22,7 +22,7 @@ VSA_TAG_TEXT, VSA_TAG_COND, VSA_TAG_AUDIO, VSA_TAG_VIDEO = 0, 1, 2, 3
 
 EXPORTED = (
     "vsa_h3_topk", "vsa_h3_plan_create", "vsa_h3_plan_info", "vsa_h3_plan_layout",
-    "vsa_h3_plan_tables", "vsa_h3_plan_upload", "vsa_h3_forward",
+    "vsa_h3_plan_tables", "vsa_h3_plan_upload", "vsa_h3_forward", "vsa_h3_forward_timed",
     "vsa_h3_oneshot_workspace_bytes", "vsa_h3_forward_oneshot", "vsa_h3_plan_destroy",
     "vsa_h3_last_error", "vsa_h3_version",
 )
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.vsa_h3_plan_upload.argtypes = [_P, _P, ctypes.c_uint64, _P]
         L.vsa_h3_forward.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P,
                                      ctypes.c_uint64, _P]
+        L.vsa_h3_forward_timed.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P,
+                                           ctypes.c_uint64, _P, ctypes.POINTER(_P)]
         L.vsa_h3_oneshot_workspace_bytes.argtypes = [_I64P, _I64P, ctypes.c_int64, Dims3, Dims3,
                                                      ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_double,
@@ -164,6 +166,15 @@ def vsa_h3_forward(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr: int,
                    stream: int) -> None:
     check(lib().vsa_h3_forward(plan, q_ptr, k_ptr, v_ptr, gate_ptr, io_dtype, out_ptr, sel_ptr,
                                workspace_ptr, workspace_bytes, stream))
+
+
+def vsa_h3_forward_timed(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr: int,
+                         io_dtype: int, out_ptr: int, sel_ptr, workspace_ptr: int,
+                         workspace_bytes: int, stream: int, events) -> None:
+    """``events``: 4 hipEvent_t handles (ints) recorded at the stage boundaries."""
+    arr = (_P * 4)(*events) if events is not None else None
+    check(lib().vsa_h3_forward_timed(plan, q_ptr, k_ptr, v_ptr, gate_ptr, io_dtype, out_ptr,
+                                     sel_ptr, workspace_ptr, workspace_bytes, stream, arr))
 
 
 def vsa_h3_oneshot_workspace_bytes(token_tags, position_ids, grid, tile, heads, head_dim,

@@ -185,6 +185,14 @@ vsa_status vsa_h3_plan_upload(const vsa_h3_plan* plan, void* workspace, uint64_t
 vsa_status vsa_h3_forward(const vsa_h3_plan* plan, const void* q, const void* k, const void* v,
                           const void* gate, vsa_dtype io_dtype, void* out, int32_t* sel_idx,
                           void* workspace, uint64_t workspace_bytes, void* stream) {
+  return vsa_h3_forward_timed(plan, q, k, v, gate, io_dtype, out, sel_idx, workspace,
+                              workspace_bytes, stream, nullptr);
+}
+
+vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const void* k,
+                                const void* v, const void* gate, vsa_dtype io_dtype, void* out,
+                                int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
+                                void* stream, void* const* events) {
   if (!plan) {
     set_error("plan is NULL");
     return VSA_E_ARG;
@@ -235,17 +243,25 @@ vsa_status vsa_h3_forward(const vsa_h3_plan* plan, const void* q, const void* k,
   float* coarse = reinterpret_cast<float*>(ws + lo.coarse);
   int32_t* sel = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(ws + lo.sel);
 
+  auto mark = [&](int idx) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[idx]), s) : hipSuccess;
+  };
+  hipError_t err = mark(0);
+  if (err != hipSuccess) return hip_fail("hipEventRecord", err);
   vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, kt, vt, qp, kp, vp};
-  hipError_t err = vsa::launch_permute_pool(pa, s);
+  err = vsa::launch_permute_pool(pa, s);
   if (err != hipSuccess) return hip_fail("permute_pool launch", err);
+  if ((err = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
   vsa::CoarseArgs ca{qp, kp, vp, scores, coarse, sel, H, Nt, static_cast<int>(lo.ns), P, NV, topk, D};
   err = vsa::launch_coarse(ca, s);
   if (err != hipSuccess) return hip_fail("coarse launch", err);
+  if ((err = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
   vsa::FineArgs fa{q, gate, out, f32, kt, vt, coarse, perm, valid, sel, H, Nt, P, NV, topk, D};
   err = vsa::launch_fine(fa, s);
   if (err != hipSuccess) return hip_fail("fine_attn launch", err);
+  if ((err = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", err);
   return VSA_OK;
 }
 
