@@ -61,7 +61,9 @@ def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True):
                 kt_ref[j, :len(idx)] = _bf16_bits(x["k"][idx, h])
                 vt_ref[j, :len(idx)] = _bf16_bits(x["v"][idx, h])
             assert torch.equal(inter["kt"][h], kt_ref), f"K tiles head {h}"
-            assert torch.equal(inter["vt"][h], vt_ref.transpose(1, 2)), f"V^T tiles head {h}"
+            # V^T columns: inside each 16-slot group, slots 0-3, 8-11, 4-7, 12-15
+            cols = [(p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1) for p in range(64)]
+            assert torch.equal(inter["vt"][h], vt_ref.transpose(1, 2)[:, :, cols]), f"V^T tiles head {h}"
     return out, sel, plan, ws
 
 

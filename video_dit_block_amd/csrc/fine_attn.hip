@@ -12,20 +12,29 @@
 // per-tile compression output, "What was tried and not shipped").
 //
 // Design (gfx950, wave64):
-//   - one block of 4 waves per (head, query tile); wave w owns query rows
-//     16w..16w+15 of the 64-row tile; query rows are gathered straight from
-//     the packed [L][H][D] input through the tile's slot table;
+//   - one block of 2 waves per (head, query tile); wave w owns query rows
+//     32w..32w+31 of the 64-row tile, gathered straight from the packed
+//     [L][H][D] input through the tile's slot table into MFMA operand
+//     registers;
 //   - the visit list is ascending (prefix tiles 0..P-1, then the selected
 //     video tiles), so every row starts from a finite running max;
-//   - per key tile: K [64][D] and V^T [D][64] (bf16) are staged in LDS with
-//     XOR-swizzled 16-byte chunks (conflict-free MFMA operand reads), the next
-//     tile is prefetched into registers meanwhile;
-//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys are the M dimension, so
+//   - K [64][D] and V^T [D][64] of the current key tile sit in two LDS
+//     regions filled by direct global->LDS loads (global_load_lds_dwordx4,
+//     no register staging).  K(t+1) is requested as soon as S(t) is computed
+//     and V(t+1) as soon as P(t).V(t) is done, so each load overlaps about
+//     half an iteration, and four blocks per CU cover the rest;
+//   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so
 //     each lane holds one query column), online softmax in fp32 via exp2 with
-//     the 1/sqrt(D) scale folded into log2 units, P rounded to bf16;
-//   - O^T += V^T P^T on the same MFMA; the key order inside each 32-key chunk
-//     is permuted identically in both operands so that P^T is consumed
-//     straight from the S^T accumulator layout, without a shuffle.
+//     the 1/sqrt(D) scale folded into log2 units; the running max is raised
+//     only when a tile exceeds it by more than 2^8 (probabilities stay below
+//     256, exact enough for bf16 P and fp32 sums), so the O rescale is rare;
+//   - O^T += V^T P^T on the same MFMA: P^T is consumed straight from the S^T
+//     accumulator layout; V^T is stored with the keys of each 16-key group
+//     permuted (0-3, 8-11, 4-7, 12-15) so that each lane's 8 keys are one
+//     16-byte LDS read;
+//   - LDS rows use XOR-swizzled 16-byte chunks, bank-conflict free for the
+//     MFMA operand reads;
+//   - partial key tiles skip their empty 16-key chunks entirely;
 //   - blocks are mapped to the 8 XCDs so that each XCD works through its own
 //     heads, head by head, prefix (long) items first: the 32 CUs of an XCD
 //     sweep the same head's K/V, which keeps it hot in that XCD's L2.
@@ -35,6 +44,10 @@
 namespace vsa {
 
 namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
 template <typename T>
 struct IoOps;
@@ -110,184 +123,229 @@ __device__ __forceinline__ void decode_item(int b, int H, int P, int NV, int& h,
   }
 }
 
+// s_waitcnt immediate that waits for vmcnt <= N (N < 16, OR-ed in) and leaves
+// expcnt and lgkmcnt unconstrained.  The builtin, unlike inline asm, is seen
+// by the compiler's own wait-count pass, which then does not add a
+// conservative vmcnt(0) in front of the LDS reads.
+constexpr int kWaitVm = 0x0F70;
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row, conflict free
+// for the operand reads of 8 (32 banks) or 16 (64 banks) consecutive rows.
+__device__ __forceinline__ int swz128(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz256(int row) { return row & 15; }
+
 template <typename TIO, int D>
-__global__ __launch_bounds__(256, 2) void fine_attn_kernel(FineArgs a) {
-  constexpr int KCH = D / 32;        // 16-byte chunks per thread per K (or V) tile
-  constexpr int KROW = D / 8;        // 16-byte chunks per K row
-  constexpr int NB = D / 16;         // O^T blocks of 16 channels
-  __shared__ __attribute__((aligned(16))) uint16_t ks[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[D * 64];
+__global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
+                                                          const int32_t* __restrict__ valid,
+                                                          const int32_t* __restrict__ sel) {
+  constexpr int KROW = D / 8;                  // 16-byte chunks per K row
+  constexpr int TILE_BYTES = 64 * D * 2;       // one K (or V^T) tile
+  constexpr int LOADS = TILE_BYTES / 1024 / 2; // 1 KB DMA loads per wave per tile
+  constexpr int NCK = D / 16;                  // QK contraction steps
+  constexpr int NB = D / 32;                   // O^T blocks of 32 channels
+  __shared__ __attribute__((aligned(1024))) char lds_k[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_v[TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int ln = lane & 15;
+  const int hl = lane >> 5;      // lane half: k-slots 8*hl..8*hl+7 of each MFMA
+  const int l32 = lane & 31;
   const int H = a.H, Nt = a.Nt, P = a.P, NV = a.NV, topk = a.topk;
 
-  int h, i;
-  decode_item(blockIdx.x, H, P, NV, h, i);
-
-  const TIO* q = static_cast<const TIO*>(a.q);
-  const int slot_q = 16 * w + ln;
-  const int pr = a.perm[static_cast<size_t>(i) * 64 + slot_q];
+  int hd, i;
+  decode_item(blockIdx.x, H, P, NV, hd, i);
 
   // Query fragment: B operand of S^T = K Q^T (column = query, k = channel).
-  bf16x8 qf[D / 32];
+  const TIO* q = static_cast<const TIO*>(a.q);
+  const int pr = a.perm[static_cast<size_t>(i) * 64 + 32 * w + l32];
+  bf16x8 qf[NCK];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    if (pr >= 0) {
-      qf[c] = IoOps<TIO>::load8(q + (static_cast<size_t>(pr) * H + h) * D + 32 * c + 8 * g);
-    } else {
+  for (int c = 0; c < NCK; ++c) {
+    if (pr >= 0)
+      qf[c] = IoOps<TIO>::load8(q + (static_cast<size_t>(pr) * H + hd) * D + 16 * c + 8 * hl);
+    else
       qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
   }
 
   const int nlist = i < P ? Nt : P + topk;
-  const int32_t* sl = i < P ? nullptr : a.sel + (static_cast<size_t>(h) * NV + (i - P)) * topk;
-  const uint16_t* kth = a.kt + static_cast<size_t>(h) * Nt * 64 * D;
-  const uint16_t* vth = a.vt + static_cast<size_t>(h) * Nt * 64 * D;
-
+  const bool dense = i < P;
+  const int32_t* sl = sel + (dense ? 0 : (static_cast<size_t>(hd) * NV + (i - P)) * topk);
+  const char* kth = reinterpret_cast<const char*>(a.kt) + static_cast<size_t>(hd) * Nt * TILE_BYTES;
+  const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nt * TILE_BYTES;
   // Listed ids are clamped into [0, Nt): a corrupt list can give a wrong
   // result but never an out-of-bounds read.
   auto tile_at = [&](int it) -> int {
-    const int t = (sl == nullptr || it < P) ? it : sl[it - P];
+    const int t = (dense || it < P) ? it : sl[it - P];
     return min(max(t, 0), Nt - 1);
   };
 
-  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
-  f32x4 oacc[NB];
+  // Per-lane source offsets of the DMA loads: the lane that fills LDS chunk p
+  // fetches the global chunk that the swizzle places there.
+  int koff[LOADS], voff[LOADS];
 #pragma unroll
-  for (int n = 0; n < NB; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < LOADS; ++e) {
+    const int p = (w * LOADS + e) * 64 + lane;
+    const int key = p / KROW, pc = p % KROW;
+    const int kswz = D == 128 ? swz256(key) : swz128(key);
+    koff[e] = key * (D * 2) + ((pc ^ kswz) << 4);
+    const int d = p >> 3, pv = p & 7;
+    voff[e] = d * 128 + ((pv ^ swz128(d)) << 4);
+  }
+// Block barrier without the workgroup fence of __syncthreads(): the fence
+// would also wait for every outstanding global->LDS load, which this loop
+// keeps in flight on purpose.  LDS reads are drained first (so no wave's
+// pending read can race the next DMA into that region) and DMA completion is
+// awaited explicitly (kWaitVm) before the barriers that publish a tile.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+#define VSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+#define VSA_LOAD_TILE(LDSBUF, SRC, OFF)                                                        \
+  _Pragma("unroll") for (int e = 0; e < LOADS; ++e) {                                          \
+    __builtin_amdgcn_global_load_lds((gbl_void*)((SRC) + OFF[e]),                            \
+                                     (lds_void*)(LDSBUF + (w * LOADS + e) * 1024),             \
+                                     16, 0, 0);                                                \
+  }
+
+  // Per-lane LDS read offsets of the MFMA operands.
+  const int kswz_r = D == 128 ? swz256(l32) : swz128(l32);
+  const int vswz_r = swz128(l32);
+
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  f32x16 oacc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
-  // Register prefetch of the next K / V^T tile (16-byte chunks, coalesced).
-  u32x4 kr[KCH], vr[KCH];
   int j = tile_at(0);
-  {
-    const u32x4* kg = reinterpret_cast<const u32x4*>(kth + static_cast<size_t>(j) * 64 * D);
-    const u32x4* vg = reinterpret_cast<const u32x4*>(vth + static_cast<size_t>(j) * 64 * D);
-#pragma unroll
-    for (int e = 0; e < KCH; ++e) {
-      kr[e] = kg[e * 256 + tid];
-      vr[e] = vg[e * 256 + tid];
-    }
-  }
-  for (int it = 0; it < nlist; ++it) {
-    const int nj = a.valid[j];
-#pragma unroll
-    for (int e = 0; e < KCH; ++e) {
-      const int id = e * 256 + tid;
-      const int key = id / KROW, ch = id % KROW;
-      reinterpret_cast<u32x4*>(ks)[key * KROW + (ch ^ (key & (KROW - 1)))] = kr[e];
-      const int d = id >> 3, cv = id & 7;
-      reinterpret_cast<u32x4*>(vs)[d * 8 + (cv ^ ((d >> 1) & 7))] = vr[e];
-    }
-    __syncthreads();
-    // Next tile (the last iteration re-reads the current one instead of branching).
-    const int jn = it + 1 < nlist ? tile_at(it + 1) : j;
-    {
-      const u32x4* kg = reinterpret_cast<const u32x4*>(kth + static_cast<size_t>(jn) * 64 * D);
-      const u32x4* vg = reinterpret_cast<const u32x4*>(vth + static_cast<size_t>(jn) * 64 * D);
-#pragma unroll
-      for (int e = 0; e < KCH; ++e) {
-        kr[e] = kg[e * 256 + tid];
-        vr[e] = vg[e * 256 + tid];
-      }
-    }
+  VSA_LOAD_TILE(lds_k, kth + static_cast<size_t>(j) * TILE_BYTES, koff);
+  VSA_LOAD_TILE(lds_v, vth + static_cast<size_t>(j) * TILE_BYTES, voff);
 
-    // S^T block b: keys 16b..16b+15 (rows) x this wave's 16 queries (columns).
-    f32x4 sacc[4];
+  for (int it = 0; it < nlist; ++it) {
+    const int nj = valid[j];
+    const int nchunk = (nj + 15) >> 4;   // 16-key chunks holding valid keys
+    // K(t) landed (V(t) may still be in flight).
+    __builtin_amdgcn_s_waitcnt(kWaitVm | LOADS);
+    VSA_BARRIER();
+
+    // Block 1 (keys 32..63) is computed only if it holds valid keys; its
+    // registers are read only for chunks below nchunk.
+    f32x16 sacc[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = 16 * b + ln;
+    for (int b = 0; b < 2; ++b) {
+      if (b == 0 || nj > 32) {
+        const char* krow = lds_k + (32 * b + l32) * (D * 2);
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const int ch = (4 * c + g) ^ (key & (KROW - 1));
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + key * D + ch * 8);
-        sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sacc[b], 0, 0, 0);
+        for (int c = 0; c < NCK; ++c) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (((2 * c + hl) ^ kswz_r) << 4));
+          sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? f32x16{} : sacc[b],
+                                                            0, 0, 0);
+        }
       }
     }
-    // Lane holds keys 16b + 4g + r of query column ln.
-    if (nj < 64) {
+    VSA_BARRIER();  // every wave is done with K(t)
+    // The last iteration re-requests its own tile, so that every iteration
+    // issues the same loads and the wait counts below stay exact.
+    const int jn = it + 1 < nlist ? tile_at(it + 1) : j;
+    VSA_LOAD_TILE(lds_k, kth + static_cast<size_t>(jn) * TILE_BYTES, koff);
+
+    // Lane holds keys 32b + 8(r/4) + 4hl + r%4 of query column l32; 16-key
+    // chunk e is registers 8(e%2)..8(e%2)+7 of block e/2.
+    if (nj & 15) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * b + 4 * g + r >= nj) sacc[b][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          if (32 * b + 8 * (r >> 2) + 4 * hl + (r & 3) >= nj) sacc[b][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int e = 0; e < 4; ++e) {
+      if (e < nchunk) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[b][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float p[4][4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[b][r] = __builtin_amdgcn_exp2f(fmaf(sacc[b][r], scale_log2, -m_new));
-        psum += p[b][r];
-      }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int n = 0; n < NB; ++n) oacc[n] *= alpha;
-
-    // O^T += V^T P^T over two 32-key chunks.  k-slot 8g+e <-> key
-    // 32*c2 + 16*(e/4) + 4g + e%4, in both operands.
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      u32x4 pu;
-      pu.x = pack_bf16x2(p[2 * c2][0], p[2 * c2][1]);
-      pu.y = pack_bf16x2(p[2 * c2][2], p[2 * c2][3]);
-      pu.z = pack_bf16x2(p[2 * c2 + 1][0], p[2 * c2 + 1][1]);
-      pu.w = pack_bf16x2(p[2 * c2 + 1][2], p[2 * c2 + 1][3]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pu);
-      const int c8a = 8 * c2 + g, c8b = 8 * c2 + 4 + g;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int d = 16 * n + ln;
-        const uint16_t* row = vs + d * 64;
-        const int sw = (d >> 1) & 7;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(row + (((c8a >> 1) ^ sw) * 8 + (c8a & 1) * 4));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + (((c8b >> 1) ^ sw) * 8 + (c8b & 1) * 4));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[n], 0, 0, 0);
+        for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sacc[e >> 1][8 * (e & 1) + r]);
       }
     }
-    __syncthreads();
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_tile = mx * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) oacc[n] *= alpha;
+    }
+
+    bf16x8 pf[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (e < nchunk) {
+        float pv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          pv[r] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 1][8 * (e & 1) + r], scale_log2, -m_run));
+          psum += pv[r];
+        }
+        u32x4 pu;
+        pu.x = pack_bf16x2(pv[0], pv[1]);
+        pu.y = pack_bf16x2(pv[2], pv[3]);
+        pu.z = pack_bf16x2(pv[4], pv[5]);
+        pu.w = pack_bf16x2(pv[6], pv[7]);
+        pf[e] = __builtin_bit_cast(bf16x8, pu);
+      }
+    }
+    l_run += psum;
+
+    // V(t) landed (K(t+1) may still be in flight).
+    __builtin_amdgcn_s_waitcnt(kWaitVm | LOADS);
+    VSA_BARRIER();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (e < nchunk) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const char* vrow = lds_v + (32 * n + l32) * 128;
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + (((2 * e + hl) ^ vswz_r) << 4));
+          oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[e], oacc[n], 0, 0, 0);
+        }
+      }
+    }
+    VSA_BARRIER();  // every wave is done with V(t)
+    VSA_LOAD_TILE(lds_v, vth + static_cast<size_t>(jn) * TILE_BYTES, voff);
     j = jn;
   }
+  // No global->LDS load may still be in flight when the block's LDS is released.
+  __builtin_amdgcn_s_waitcnt(kWaitVm);
+#undef VSA_LOAD_TILE
+#undef VSA_BARRIER
 
   // Epilogue: normalise, add gate * coarse, store at the packed row.
-  l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (pr >= 0) {
     const float inv = 1.0f / l_run;
-    const float* cg = a.coarse + (static_cast<size_t>(h) * Nt + i) * D;
-    const size_t rowoff = (static_cast<size_t>(pr) * H + h) * D;
+    const float* cg = a.coarse + (static_cast<size_t>(hd) * Nt + i) * D;
+    const size_t rowoff = (static_cast<size_t>(pr) * H + hd) * D;
     const TIO* gate = static_cast<const TIO*>(a.gate) + rowoff;
     TIO* out = static_cast<TIO*>(a.out) + rowoff;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const int d0 = 16 * n + 4 * g;
-      const float4 cc = *reinterpret_cast<const float4*>(cg + d0);
-      float gv[4];
-      IoOps<TIO>::load4(gate + d0, gv);
-      float res[4];
-      res[0] = fmaf(gv[0], cc.x, oacc[n][0] * inv);
-      res[1] = fmaf(gv[1], cc.y, oacc[n][1] * inv);
-      res[2] = fmaf(gv[2], cc.z, oacc[n][2] * inv);
-      res[3] = fmaf(gv[3], cc.w, oacc[n][3] * inv);
-      IoOps<TIO>::store4(out + d0, res);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * n + 8 * g4 + 4 * hl;
+        const float4 cc = *reinterpret_cast<const float4*>(cg + d0);
+        float gv[4];
+        IoOps<TIO>::load4(gate + d0, gv);
+        float res[4];
+        res[0] = fmaf(gv[0], cc.x, oacc[n][4 * g4 + 0] * inv);
+        res[1] = fmaf(gv[1], cc.y, oacc[n][4 * g4 + 1] * inv);
+        res[2] = fmaf(gv[2], cc.z, oacc[n][4 * g4 + 2] * inv);
+        res[3] = fmaf(gv[3], cc.w, oacc[n][4 * g4 + 3] * inv);
+        IoOps<TIO>::store4(out + d0, res);
+      }
     }
   }
 }
@@ -295,7 +353,8 @@ __global__ __launch_bounds__(256, 2) void fine_attn_kernel(FineArgs a) {
 template <typename TIO, int D>
 hipError_t launch(const FineArgs& a, hipStream_t stream) {
   const int blocks = a.H * a.Nt;
-  hipLaunchKernelGGL((fine_attn_kernel<TIO, D>), dim3(blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fine_attn_kernel<TIO, D>), dim3(blocks), dim3(128), 0, stream, a, a.valid,
+                     a.sel);
   return hipGetLastError();
 }
 

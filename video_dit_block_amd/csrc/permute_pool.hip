@@ -8,8 +8,10 @@
 // One block per (head, tile).  The tile's 64 slots of q, k and v are staged
 // in LDS (pad slots zero), then
 //   - k is written to Kt[h][tile][slot][d] (bf16),
-//   - v is written transposed to Vt[h][tile][d][slot] (bf16), the layout the
-//     fine kernel's P.V operand wants,
+//   - v is written transposed to Vt[h][tile][d][pos] (bf16), the layout the
+//     fine kernel's P.V operand wants: inside each group of 16 slots the
+//     storage order is slots 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the slot
+//     swapped), so that the 8 keys one MFMA lane contracts over are adjacent;
 //   - q, k, v are mean-pooled per channel: a sequential fp32 sum over the
 //     valid slots in slot order, then one correctly rounded division by the
 //     count.  That fixed order makes the pooled values, and therefore the
@@ -87,18 +89,21 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
       *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
     }
   }
-  // Vt: [d][slot] bf16, 16-byte chunks of 8 slots.
+  // Vt: [d][pos] bf16, 16-byte chunks of 8 positions.  Positions p0..p0+7
+  // (p0 = 8m) hold slots 16(m/2) + 4(m%2) + {0..3} and the same + 8.
   {
     uint16_t* dst = vt + tile_base * 64 * D;
     for (int c = tid; c < D * 8; c += blockDim.x) {
       const int d = c % D;
-      const int s0 = (c / D) * 8;
+      const int m = c / D;
+      const int sa = 16 * (m >> 1) + 4 * (m & 1);
+      const int sb = sa + 8;
       uint4 o;
-      o.x = pack_bf16x2(to_f32(lds[2][s0 + 0][d]), to_f32(lds[2][s0 + 1][d]));
-      o.y = pack_bf16x2(to_f32(lds[2][s0 + 2][d]), to_f32(lds[2][s0 + 3][d]));
-      o.z = pack_bf16x2(to_f32(lds[2][s0 + 4][d]), to_f32(lds[2][s0 + 5][d]));
-      o.w = pack_bf16x2(to_f32(lds[2][s0 + 6][d]), to_f32(lds[2][s0 + 7][d]));
-      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(d) * 64 + s0) = o;
+      o.x = pack_bf16x2(to_f32(lds[2][sa + 0][d]), to_f32(lds[2][sa + 1][d]));
+      o.y = pack_bf16x2(to_f32(lds[2][sa + 2][d]), to_f32(lds[2][sa + 3][d]));
+      o.z = pack_bf16x2(to_f32(lds[2][sb + 0][d]), to_f32(lds[2][sb + 1][d]));
+      o.w = pack_bf16x2(to_f32(lds[2][sb + 2][d]), to_f32(lds[2][sb + 3][d]));
+      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(d) * 64 + 8 * m) = o;
     }
   }
 }
