@@ -147,7 +147,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   __shared__ __attribute__((aligned(1024))) char lds_v[TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int lane = tid & 63;
   const int hl = lane >> 5;      // lane half: k-slots 8*hl..8*hl+7 of each MFMA
   const int l32 = lane & 31;
@@ -181,16 +181,31 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   };
 
   // Per-lane source offsets of the DMA loads: the lane that fills LDS chunk p
-  // fetches the global chunk that the swizzle places there.
-  int koff[LOADS], voff[LOADS];
+  // fetches the global chunk that the swizzle places there.  The swizzle term
+  // repeats every KREP (VREP) loads, so a few base offsets plus a constant
+  // stride cover all of them.  Wave w fills K rows 32w..32w+31.
+  constexpr int KREP = D == 128 ? 4 : 2;
+  constexpr int KSTEP = D == 128 ? 16 * 256 : 16 * 128;   // rows per KREP loads x row bytes
+  constexpr int KROWS_PER_LOAD = 1024 / (D * 2);
+  constexpr int VREP = 2;
+  constexpr int VSTEP = 16 * 128;
+  int kbase[KREP], vbase[VREP], vmin[VREP];
 #pragma unroll
-  for (int e = 0; e < LOADS; ++e) {
+  for (int e = 0; e < KREP; ++e) {
     const int p = (w * LOADS + e) * 64 + lane;
     const int key = p / KROW, pc = p % KROW;
     const int kswz = D == 128 ? swz256(key) : swz128(key);
-    koff[e] = key * (D * 2) + ((pc ^ kswz) << 4);
+    kbase[e] = key * (D * 2) + ((pc ^ kswz) << 4);
+  }
+#pragma unroll
+  for (int e = 0; e < VREP; ++e) {
+    const int p = (w * LOADS + e) * 64 + lane;
     const int d = p >> 3, pv = p & 7;
-    voff[e] = d * 128 + ((pv ^ swz128(d)) << 4);
+    const int lc = pv ^ swz128(d);               // logical chunk: positions 8lc..8lc+7
+    vbase[e] = d * 128 + (lc << 4);
+    // The P.V step reads whole 16-key groups (pad slots included, which are
+    // zero in memory): a chunk is needed iff its group holds a valid key.
+    vmin[e] = 16 * (lc >> 1);
   }
 // Block barrier without the workgroup fence of __syncthreads(): the fence
 // would also wait for every outstanding global->LDS load, which this loop
@@ -199,12 +214,31 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 // awaited explicitly (kWaitVm) before the barriers that publish a tile.  The
 // memory clobber keeps the compiler from moving memory accesses across it.
 #define VSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-#define VSA_LOAD_TILE(LDSBUF, SRC, OFF)                                                        \
+// K: only the loads whose rows hold valid keys (a count uniform per wave).
+// Scores of rows not loaded are never used: empty 16-key chunks are skipped
+// and pad keys inside a chunk are overwritten with -inf.
+// V^T: every load is issued, so that its count stays fixed, but lanes whose
+// chunk lies in a 16-key group without valid keys stay idle; P.V never reads
+// those groups, so their stale contents (possibly non-finite) cannot leak.
+#define VSA_LOAD_K(SRC, NKL)                                                                  \
   _Pragma("unroll") for (int e = 0; e < LOADS; ++e) {                                          \
-    __builtin_amdgcn_global_load_lds((gbl_void*)((SRC) + OFF[e]),                            \
-                                     (lds_void*)(LDSBUF + (w * LOADS + e) * 1024),             \
-                                     16, 0, 0);                                                \
+    if (e < (NKL))                                                                             \
+      __builtin_amdgcn_global_load_lds(                                                        \
+          (gbl_void*)((SRC) + (e / KREP) * KSTEP + kbase[e % KREP]),                           \
+          (lds_void*)(lds_k + (w * LOADS + e) * 1024), 16, 0, 0);                              \
   }
+#define VSA_LOAD_V(SRC, NJ)                                                                   \
+  _Pragma("unroll") for (int e = 0; e < LOADS; ++e) {                                          \
+    if (vmin[e % VREP] < (NJ))                                                                 \
+      __builtin_amdgcn_global_load_lds(                                                        \
+          (gbl_void*)((SRC) + (e / VREP) * VSTEP + vbase[e % VREP]),                           \
+          (lds_void*)(lds_v + (w * LOADS + e) * 1024), 16, 0, 0);                              \
+  }
+  // K loads this wave issues for a tile with n valid keys.
+  auto k_loads = [&](int n) -> int {
+    const int rows = n - 32 * w;
+    return rows <= 0 ? 0 : min(LOADS, (rows + KROWS_PER_LOAD - 1) / KROWS_PER_LOAD);
+  };
 
   // Per-lane LDS read offsets of the MFMA operands.
   const int kswz_r = D == 128 ? swz256(l32) : swz128(l32);
@@ -220,11 +254,11 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   float l_run = 0.0f;
 
   int j = tile_at(0);
-  VSA_LOAD_TILE(lds_k, kth + static_cast<size_t>(j) * TILE_BYTES, koff);
-  VSA_LOAD_TILE(lds_v, vth + static_cast<size_t>(j) * TILE_BYTES, voff);
+  int nj = valid[j];
+  VSA_LOAD_K(kth + static_cast<size_t>(j) * TILE_BYTES, k_loads(nj));
+  VSA_LOAD_V(vth + static_cast<size_t>(j) * TILE_BYTES, nj);
 
   for (int it = 0; it < nlist; ++it) {
-    const int nj = valid[j];
     const int nchunk = (nj + 15) >> 4;   // 16-key chunks holding valid keys
     // K(t) landed (V(t) may still be in flight).
     __builtin_amdgcn_s_waitcnt(kWaitVm | LOADS);
@@ -249,7 +283,9 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     // The last iteration re-requests its own tile, so that every iteration
     // issues the same loads and the wait counts below stay exact.
     const int jn = it + 1 < nlist ? tile_at(it + 1) : j;
-    VSA_LOAD_TILE(lds_k, kth + static_cast<size_t>(jn) * TILE_BYTES, koff);
+    const int njn = valid[jn];
+    const int kl_next = k_loads(njn);
+    VSA_LOAD_K(kth + static_cast<size_t>(jn) * TILE_BYTES, kl_next);
 
     // Lane holds keys 32b + 8(r/4) + 4hl + r%4 of query column l32; 16-key
     // chunk e is registers 8(e%2)..8(e%2)+7 of block e/2.
@@ -300,8 +336,18 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     }
     l_run += psum;
 
-    // V(t) landed (K(t+1) may still be in flight).
-    __builtin_amdgcn_s_waitcnt(kWaitVm | LOADS);
+    // V(t) landed (the kl_next loads of K(t+1) may still be in flight).
+    switch (kl_next) {
+      case 0: __builtin_amdgcn_s_waitcnt(kWaitVm | 0); break;
+      case 1: __builtin_amdgcn_s_waitcnt(kWaitVm | 1); break;
+      case 2: __builtin_amdgcn_s_waitcnt(kWaitVm | 2); break;
+      case 3: __builtin_amdgcn_s_waitcnt(kWaitVm | 3); break;
+      case 4: __builtin_amdgcn_s_waitcnt(kWaitVm | 4); break;
+      case 5: __builtin_amdgcn_s_waitcnt(kWaitVm | 5); break;
+      case 6: __builtin_amdgcn_s_waitcnt(kWaitVm | 6); break;
+      case 7: __builtin_amdgcn_s_waitcnt(kWaitVm | 7); break;
+      default: __builtin_amdgcn_s_waitcnt(kWaitVm | 8); break;
+    }
     VSA_BARRIER();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -315,12 +361,14 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
       }
     }
     VSA_BARRIER();  // every wave is done with V(t)
-    VSA_LOAD_TILE(lds_v, vth + static_cast<size_t>(jn) * TILE_BYTES, voff);
+    VSA_LOAD_V(vth + static_cast<size_t>(jn) * TILE_BYTES, njn);
     j = jn;
+    nj = njn;
   }
   // No global->LDS load may still be in flight when the block's LDS is released.
   __builtin_amdgcn_s_waitcnt(kWaitVm);
-#undef VSA_LOAD_TILE
+#undef VSA_LOAD_K
+#undef VSA_LOAD_V
 #undef VSA_BARRIER
 
   // Epilogue: normalise, add gate * coarse, store at the packed row.
