@@ -159,6 +159,9 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   // Query fragment: B operand of S^T = K Q^T (column = query, k = channel).
   const TIO* q = static_cast<const TIO*>(a.q);
   const int pr = a.perm[static_cast<size_t>(i) * 64 + 32 * w + l32];
+  // A wave whose 32 query rows are all pad slots (the second half of a tile
+  // with at most 32 valid tokens) only takes part in the loads and barriers.
+  const bool active = 32 * w < valid[i];
   bf16x8 qf[NCK];
 #pragma unroll
   for (int c = 0; c < NCK; ++c) {
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   VSA_LOAD_V(vth + static_cast<size_t>(j) * TILE_BYTES, nj);
 
   for (int it = 0; it < nlist; ++it) {
-    const int nchunk = (nj + 15) >> 4;   // 16-key chunks holding valid keys
+    const int nchunk = active ? (nj + 15) >> 4 : 0;   // 16-key chunks to process
     // K(t) landed (V(t) may still be in flight).
     __builtin_amdgcn_s_waitcnt(kWaitVm | LOADS);
     VSA_BARRIER();
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     f32x16 sacc[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      if (b == 0 || nj > 32) {
+      if (active && (b == 0 || nj > 32)) {
         const char* krow = lds_k + (32 * b + l32) * (D * 2);
 #pragma unroll
         for (int c = 0; c < NCK; ++c) {
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 
     // Lane holds keys 32b + 8(r/4) + 4hl + r%4 of query column l32; 16-key
     // chunk e is registers 8(e%2)..8(e%2)+7 of block e/2.
-    if (nj & 15) {
+    if (active && (nj & 15)) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
