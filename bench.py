@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk (MI355X dense b
 PEAK_HBM_GBS = 8000.0
 METRIC = "VSA-H3 fwd ms and effective TFLOP/s (% bf16 MFMA peak) at 73.6k tokens"
 FINE_SOURCES = ["video_dit_block_amd/csrc/fine_attn.hip", "video_dit_block_amd/csrc/device.hpp",
-                "video_dit_block_amd/csrc/kernels.hpp"]
+                "video_dit_block_amd/csrc/kernels.hpp", "video_dit_block_amd/csrc/plan.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_768p10s_traffic.json")
 
 
@@ -100,15 +100,18 @@ def sources_digest(paths):
     return h.hexdigest()
 
 
-def load_traffic():
-    """HBM bytes per fine-attention launch from the committed counter summary,
-    or None if it is missing or was taken on a different kernel source."""
+def load_traffic(launches: int):
+    """HBM bytes per fine-attention launch (the forward's fine-branch bytes over
+    its key-chunk launches) from the committed counter summary, or None if it
+    is missing or was taken on a different kernel source or launch count."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_sources_sha256") != sources_digest(FINE_SOURCES):
+        return None
+    if t.get("launches_per_forward") != launches:
         return None
     return t.get("bytes_per_launch")
 
@@ -221,6 +224,9 @@ def main():
     tflops = total / (ms_per_step * 1e-3) / 1e12
     fine_ms = float(stage[:, 2].mean())
     fine_tflops = alg_fine / (fine_ms * 1e-3) / 1e12
+    # The fine branch runs as one launch per key chunk; the stage events span
+    # all of them, so per launch: the forward's flops and time over the count.
+    launches = max(plan.num_chunks, 1)
 
     rec = {
         "metric": METRIC,
@@ -250,9 +256,11 @@ def main():
             "bound": "mfma", "kernel": "fine_attn_kernel",
             "achieved": round(fine_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(fine_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(),
-            "algorithmic_flops_per_launch": alg_fine,
-            "avg_launch_ms": round(fine_ms, 4),
+            "traffic": load_traffic(launches),
+            "launches_per_forward": launches,
+            "key_chunk_tiles": plan.chunk_tiles,
+            "algorithmic_flops_per_launch": alg_fine / launches,
+            "avg_launch_ms": round(fine_ms / launches, 4),
         },
     }
     if not args.no_cpu_baseline and not args.profile_pass:

@@ -66,6 +66,8 @@ typedef struct {
   int64_t topk;              /* video key tiles kept per video query tile (0 if NV == 0) */
   int32_t heads, head_dim;
   uint64_t workspace_bytes;  /* bytes the workspace must hold */
+  int32_t chunk_tiles;       /* key tiles per fine-branch key chunk */
+  int32_t num_chunks;        /* key chunks, ceil(num_tiles / chunk_tiles); 0 if num_tiles == 0 */
 } vsa_h3_info;
 
 /* Byte offsets of the intermediates inside the workspace (each 256-aligned).
@@ -86,6 +88,10 @@ typedef struct {
   uint64_t sel;     /* int32 [H][NV][topk]: selected video key tiles, ascending */
   uint64_t total;   /* == vsa_h3_info.workspace_bytes */
   int64_t scores_row_stride;  /* Ns */
+  uint64_t chunk_offsets;  /* int32 [H][NV][num_chunks + 1] (only if num_chunks > 1): entry c
+                              counts the selected tiles of the row with id < c * chunk_tiles */
+  uint64_t state;   /* fp32 fine-branch state between key chunks (only if num_chunks > 1);
+                       internal layout */
 } vsa_h3_ws_layout;
 
 /* Top-k rule of VSA-H3 evaluated in IEEE double as written; 0 when
@@ -112,6 +118,20 @@ vsa_status vsa_h3_plan_create(const int64_t* token_tags, const int64_t* position
                               int32_t head_dim, double sparsity, vsa_h3_plan** plan_out);
 
 vsa_status vsa_h3_plan_info(const vsa_h3_plan* plan, vsa_h3_info* out);
+
+/* Key chunking of the fine branch (a schedule choice; the result does not
+ * depend on it beyond fp32 rounding of the running softmax state).  Each
+ * query tile visits its key tiles in ascending id order; the visit list is
+ * cut at multiples of chunk_tiles and the chunks run as consecutive kernel
+ * launches, so that all query tiles of a head sweep one chunk of its K/V
+ * together while it stays cached (L2 and Infinity Cache).  The running max, running
+ * sum and unnormalised output of every query row pass between launches
+ * through the workspace, in fp32.
+ *   chunk_tiles  0 picks the default (chunks of at most 10 MiB of K+V per
+ *                head, balanced); otherwise the chunk length in key tiles.
+ * The workspace size changes: call before sizing and uploading a workspace.
+ * VSA_E_ARG if chunk_tiles < 0 or if it gives more than 63 chunks. */
+vsa_status vsa_h3_plan_set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles);
 vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out);
 
 /* Host copies of the plan tables into caller-provided host buffers (any may

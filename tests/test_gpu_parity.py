@@ -30,9 +30,22 @@ def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
     return x.to(torch.bfloat16).view(torch.int16)
 
 
-def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True):
+def check_chunk_offsets(plan, ws, sel):
+    """Entry c of a row counts its selected tiles with id < c * chunk_tiles."""
+    if plan.num_chunks <= 1 or plan.num_video_tiles == 0:
+        return
+    H, NV, C = plan.heads, plan.num_video_tiles, plan.num_chunks
+    got = plan.view(ws, "chunk_offsets", torch.int32, (H, NV, C + 1)).cpu().numpy()
+    bounds = np.minimum(np.arange(C + 1) * plan.chunk_tiles, plan.num_tiles)
+    s = sel.cpu().numpy()
+    want = (s[:, :, :, None] < bounds[None, None, None, :]).sum(axis=2)
+    assert np.array_equal(got, want)
+
+
+def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True, plan=None):
     """Run the GPU forward and compare everything with the oracle on `heads`."""
-    out, sel, plan, ws = run(x, w.grid, sparsity)
+    out, sel, plan, ws = run(x, w.grid, sparsity, plan=plan)
+    check_chunk_offsets(plan, ws, sel)
     H = w.heads
     heads = list(range(H)) if heads is None else heads
     g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
@@ -106,6 +119,35 @@ def test_layouts_full_parity(name, H, D, io, prefix, grid, s, order):
     full_check(w, x, s)
 
 
+LAYOUT_BY_NAME = {l[0]: l for l in LAYOUTS}
+CHUNKED = [("odd_bf16_d128_h8", 1), ("odd_bf16_d128_h8", 7), ("video_only_h8", 1),
+           ("video_only_h8", 3), ("odd_f32_d64_h3", 2), ("prefix_only_h2", 2),
+           ("d128_h8_s1", 4), ("d128_h8_s0", 5), ("single_tile_h4", 1)]
+
+
+@pytest.mark.parametrize("name,ch", CHUNKED, ids=[f"{n}-ch{c}" for n, c in CHUNKED])
+def test_key_chunked_launches_match_oracle_and_single_launch(name, ch):
+    """Key-chunked fine branch: the same visits in the same order as one launch,
+    with the running state passed through memory in fp32, so the result must
+    equal the single-launch result bit for bit (and the oracle to tolerance).
+    chunk_tiles 1 on the video-only layout leaves some query tiles with no work
+    in the first chunk (their initial state is stored) and in later ones (the
+    launch leaves their state untouched)."""
+    _, H, D, io, prefix, grid, s, order = LAYOUT_BY_NAME[name]
+    w = Workload(name, H, D, io, prefix, grid, s)
+    say(f"case {name}: chunk_tiles={ch}")
+    x = make_inputs(w, seed=5, video_order=order)
+    plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, H, D, s, chunk_tiles=ch)
+    nt = plan.num_tiles
+    assert plan.num_chunks == -(-nt // min(ch, nt))
+    out, sel, _, _ = full_check(w, x, s, plan=plan)
+    single = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, H, D, s, chunk_tiles=nt)
+    assert single.num_chunks == 1
+    out1, sel1, _, _ = run(x, w.grid, s, plan=single)
+    assert torch.equal(sel, sel1)
+    assert torch.equal(out, out1)
+
+
 def test_empty_sequence_is_a_noop():
     plan = vsa.Plan(np.zeros(0, np.int64), np.zeros((0, 3), np.int64), (0, 0, 0), 2, 64, 0.5)
     x = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
@@ -135,6 +177,11 @@ def test_repeatable_and_oneshot_identical():
     out1, sel1, plan, ws = run(x, w.grid, w.sparsity)
     out2, sel2, _, _ = run(x, w.grid, w.sparsity, plan=plan)
     assert torch.equal(out1, out2) and torch.equal(sel1, sel2)
+    chunked = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, 8, 128, w.sparsity,
+                       chunk_tiles=80)
+    assert (plan.num_chunks, chunked.num_chunks) == (1, 3)
+    out4, sel4, _, _ = run(x, w.grid, w.sparsity, plan=chunked)
+    assert torch.equal(out1, out4) and torch.equal(sel1, sel4)
     xd = {n: x[n].cuda() for n in ("q", "k", "v", "gate")}
     nbytes = vsa.vsa_h3_oneshot_workspace_bytes(x["token_tags"], x["position_ids"], w.grid,
                                                 (4, 4, 4), 8, 128, w.sparsity)
@@ -164,6 +211,8 @@ def sampled_check(name, heads):
     say(f"case {name}: {w.description}; oracle heads {heads}")
     x = make_inputs(w)
     out, sel, plan, ws = run(x, w.grid, w.sparsity)
+    assert plan.num_chunks > 1
+    check_chunk_offsets(plan, ws, sel)
     g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
     topk = oracle.topk_count(g.NV, w.sparsity)
     sel_all = sel.cpu().numpy()

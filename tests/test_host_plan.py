@@ -95,7 +95,9 @@ def test_workspace_layout_aligned_disjoint_and_64bit():
     regions = [("perm", Nt * 64 * 4), ("valid", Nt * 4), ("kt", H * Nt * 64 * D * 2),
                ("vt", H * Nt * 64 * D * 2), ("qp", H * Nt * D * 4), ("kp", H * Nt * D * 4),
                ("vp", H * Nt * D * 4), ("scores", H * Nt * ns * 4), ("coarse", H * Nt * D * 4),
-               ("sel", H * NV * k * 4)]
+               ("sel", H * NV * k * 4), ("chunk_offsets", H * NV * (p.num_chunks + 1) * 4),
+               ("state", H * Nt * 2 * 64 * (D // 2 + 4) * 4)]
+    assert p.num_chunks > 1
     spans = []
     for n, size in regions:
         off = getattr(lo, n)
@@ -107,6 +109,51 @@ def test_workspace_layout_aligned_disjoint_and_64bit():
     assert spans[-1][1] <= lo.total == p.workspace_bytes
     assert lo.scores_row_stride == ns
     assert lo.total > 2 ** 32          # 64-bit offsets are needed at this size
+
+
+@pytest.mark.parametrize("name,chunk_tiles,num_chunks", [
+    ("768p10s", 319, 4),          # 1,276 tiles, head_dim 128: at most 320 tiles (10 MiB) per chunk
+    ("768p15s_smooth", 302, 6),   # 1,812 tiles
+    ("480p5s", 236, 1),           # 236 tiles: one chunk
+    ("tiny", 9, 1),               # 9 tiles, head_dim 64: one chunk
+])
+def test_default_key_chunks(name, chunk_tiles, num_chunks):
+    w = WORKLOADS[name]
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    assert (p.chunk_tiles, p.num_chunks) == (chunk_tiles, num_chunks)
+    assert p.chunk_tiles * 2 * 64 * w.head_dim * 2 <= 10 << 20
+    assert (p.num_chunks - 1) * p.chunk_tiles < p.num_tiles <= p.num_chunks * p.chunk_tiles
+    if num_chunks == 1:
+        # a single launch needs neither the chunk offsets nor the running state
+        assert p.layout.total <= p.layout.state + 256
+
+
+def test_set_chunk_tiles_resizes_the_workspace_and_checks_its_argument():
+    w = Workload("c", 2, 128, "bf16", ((TEXT, 130),), (8, 12, 16), 0.5)   # 3 + 24 tiles
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    assert p.num_chunks == 1
+    base = p.workspace_bytes
+    for ch, nc in ((1, 27), (2, 14), (26, 2), (27, 1), (1000, 1)):
+        vsa.vsa_h3_plan_set_chunk_tiles(p.handle, ch)
+        info = vsa.vsa_h3_plan_info(p.handle)
+        assert (info.chunk_tiles, info.num_chunks) == (min(ch, 27), nc)
+        lo = vsa.vsa_h3_plan_layout(p.handle)
+        if nc > 1:
+            state_bytes = 2 * 27 * 2 * 64 * (128 // 2 + 4) * 4
+            assert info.workspace_bytes >= base + state_bytes
+            assert lo.state + state_bytes <= lo.total
+        else:
+            assert info.workspace_bytes == base
+    with pytest.raises(vsa.VsaError):
+        vsa.vsa_h3_plan_set_chunk_tiles(p.handle, -1)
+    big = WORKLOADS["768p10s"]
+    tags, pos = make_layout(big)
+    p2 = vsa.Plan(tags, pos, big.grid, big.heads, big.head_dim, big.sparsity)
+    with pytest.raises(vsa.VsaError):     # 1,276 chunks > 63
+        vsa.vsa_h3_plan_set_chunk_tiles(p2.handle, 1)
+    assert _abi.lib().vsa_h3_plan_set_chunk_tiles(None, 4) == _abi.VSA_E_ARG
 
 
 def _raw_create(tags, pos, grid, tile=(4, 4, 4), heads=2, D=64, s=0.5):

@@ -25,7 +25,8 @@ from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
     VSA_TAG_VIDEO, VsaError, lib, vsa_h3_forward, vsa_h3_forward_oneshot, vsa_h3_forward_timed,
     vsa_h3_last_error,
     vsa_h3_oneshot_workspace_bytes, vsa_h3_plan_create, vsa_h3_plan_destroy, vsa_h3_plan_info,
-    vsa_h3_plan_layout, vsa_h3_plan_tables, vsa_h3_plan_upload, vsa_h3_topk, vsa_h3_version,
+    vsa_h3_plan_layout, vsa_h3_plan_set_chunk_tiles, vsa_h3_plan_tables, vsa_h3_plan_upload,
+    vsa_h3_topk, vsa_h3_version,
 )
 
 __all__ = ["Plan", "forward", "VsaError", "vsa_h3_topk", "vsa_h3_version"] + list(EXPORTED)
@@ -45,7 +46,7 @@ class Plan:
     """Tile geometry for one packed layout (host), plus per-device workspaces."""
 
     def __init__(self, token_tags, position_ids, grid, heads, head_dim, sparsity,
-                 tile=(4, 4, 4)):
+                 tile=(4, 4, 4), chunk_tiles: int = 0):
         self.token_tags = _host_i64(token_tags).reshape(-1)
         self.position_ids = _host_i64(position_ids).reshape(-1, 3)
         self.grid = tuple(int(g) for g in grid)
@@ -53,6 +54,8 @@ class Plan:
         self.sparsity = float(sparsity)
         self.handle = vsa_h3_plan_create(self.token_tags, self.position_ids, self.grid,
                                          self.tile, heads, head_dim, sparsity)
+        if chunk_tiles:
+            vsa_h3_plan_set_chunk_tiles(self.handle, chunk_tiles)
         self.info = vsa_h3_plan_info(self.handle)
         self.layout = vsa_h3_plan_layout(self.handle)
         self._ws = {}
@@ -75,6 +78,10 @@ class Plan:
     def topk(self): return self.info.topk
     @property
     def workspace_bytes(self): return self.info.workspace_bytes
+    @property
+    def chunk_tiles(self): return self.info.chunk_tiles
+    @property
+    def num_chunks(self): return self.info.num_chunks
 
     def tables(self):
         """(perm [Nt, 64], valid [Nt], tile_slot [L]) as host int32 arrays."""

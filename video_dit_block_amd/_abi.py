@@ -21,7 +21,8 @@ VSA_BF16, VSA_F32 = 0, 1
 VSA_TAG_TEXT, VSA_TAG_COND, VSA_TAG_AUDIO, VSA_TAG_VIDEO = 0, 1, 2, 3
 
 EXPORTED = (
-    "vsa_h3_topk", "vsa_h3_plan_create", "vsa_h3_plan_info", "vsa_h3_plan_layout",
+    "vsa_h3_topk", "vsa_h3_plan_create", "vsa_h3_plan_info", "vsa_h3_plan_set_chunk_tiles",
+    "vsa_h3_plan_layout",
     "vsa_h3_plan_tables", "vsa_h3_plan_upload", "vsa_h3_forward", "vsa_h3_forward_timed",
     "vsa_h3_oneshot_workspace_bytes", "vsa_h3_forward_oneshot", "vsa_h3_plan_destroy",
     "vsa_h3_last_error", "vsa_h3_version",
@@ -42,13 +43,15 @@ class Info(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int64), ("num_prefix_tiles", ctypes.c_int64),
                 ("num_video_tiles", ctypes.c_int64), ("num_tiles", ctypes.c_int64),
                 ("topk", ctypes.c_int64), ("heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64)]
+                ("head_dim", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+                ("chunk_tiles", ctypes.c_int32), ("num_chunks", ctypes.c_int32)]
 
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("perm", "valid", "kt", "vt", "qp", "kp", "vp",
                                                "scores", "coarse", "sel", "total")] + \
-               [("scores_row_stride", ctypes.c_int64)]
+               [("scores_row_stride", ctypes.c_int64), ("chunk_offsets", ctypes.c_uint64),
+                ("state", ctypes.c_uint64)]
 
 
 _lib = None
@@ -76,6 +79,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                          ctypes.POINTER(_P)]
         L.vsa_h3_plan_info.argtypes = [_P, ctypes.POINTER(Info)]
+        L.vsa_h3_plan_set_chunk_tiles.argtypes = [_P, ctypes.c_int32]
         L.vsa_h3_plan_layout.argtypes = [_P, ctypes.POINTER(WsLayout)]
         L.vsa_h3_plan_tables.argtypes = [_P, _I32P, _I32P, _I32P]
         L.vsa_h3_plan_upload.argtypes = [_P, _P, ctypes.c_uint64, _P]
@@ -138,6 +142,10 @@ def vsa_h3_plan_info(plan: int) -> Info:
     info = Info()
     check(lib().vsa_h3_plan_info(plan, ctypes.byref(info)))
     return info
+
+
+def vsa_h3_plan_set_chunk_tiles(plan: int, chunk_tiles: int) -> None:
+    check(lib().vsa_h3_plan_set_chunk_tiles(plan, int(chunk_tiles)))
 
 
 def vsa_h3_plan_layout(plan: int) -> WsLayout:

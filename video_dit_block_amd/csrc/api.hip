@@ -1,6 +1,7 @@
 // C ABI of the VSA-H3 forward: argument checks, workspace carving and the
 // launch sequence  permute+pool -> coarse scores -> softmax+top-k -> P.pool(v)
-// -> fine attention with the fused gate-combine epilogue.
+// -> fine attention (one launch per key chunk) with the fused gate-combine
+// epilogue in the last.
 #include <cstring>
 #include <list>
 #include <memory>
@@ -125,7 +126,17 @@ vsa_status vsa_h3_plan_info(const vsa_h3_plan* plan, vsa_h3_info* out) {
   out->heads = plan->heads;
   out->head_dim = plan->head_dim;
   out->workspace_bytes = plan->layout.total;
+  out->chunk_tiles = plan->chunk_tiles;
+  out->num_chunks = plan->num_chunks;
   return VSA_OK;
+}
+
+vsa_status vsa_h3_plan_set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return VSA_E_ARG;
+  }
+  return vsa::set_chunk_tiles(plan, chunk_tiles);
 }
 
 vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out) {
@@ -146,6 +157,8 @@ vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out) {
   out->sel = lo.sel;
   out->total = lo.total;
   out->scores_row_stride = lo.ns;
+  out->chunk_offsets = lo.choff;
+  out->state = lo.state;
   return VSA_OK;
 }
 
@@ -242,6 +255,9 @@ vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const vo
   float* scores = reinterpret_cast<float*>(ws + lo.scores);
   float* coarse = reinterpret_cast<float*>(ws + lo.coarse);
   int32_t* sel = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(ws + lo.sel);
+  const int nchunks = plan->num_chunks, chunk_tiles = plan->chunk_tiles;
+  int32_t* choff = reinterpret_cast<int32_t*>(ws + lo.choff);
+  float* state = reinterpret_cast<float*>(ws + lo.state);
 
   auto mark = [&](int idx) -> hipError_t {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[idx]), s) : hipSuccess;
@@ -253,12 +269,14 @@ vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const vo
   if (err != hipSuccess) return hip_fail("permute_pool launch", err);
   if ((err = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
-  vsa::CoarseArgs ca{qp, kp, vp, scores, coarse, sel, H, Nt, static_cast<int>(lo.ns), P, NV, topk, D};
+  vsa::CoarseArgs ca{qp, kp, vp, scores, coarse, sel, choff, H, Nt, static_cast<int>(lo.ns),
+                     P, NV, topk, D, nchunks, chunk_tiles};
   err = vsa::launch_coarse(ca, s);
   if (err != hipSuccess) return hip_fail("coarse launch", err);
   if ((err = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
-  vsa::FineArgs fa{q, gate, out, f32, kt, vt, coarse, perm, valid, sel, H, Nt, P, NV, topk, D};
+  vsa::FineArgs fa{q, gate, out, f32, kt, vt, coarse, perm, valid, sel, choff, state,
+                   H, Nt, P, NV, topk, D, nchunks, chunk_tiles};
   err = vsa::launch_fine(fa, s);
   if (err != hipSuccess) return hip_fail("fine_attn launch", err);
   if ((err = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", err);

@@ -16,8 +16,10 @@
 //   softmax_topk  one wave per (head, query tile): the row lives in
 //                 registers; an MSB-first bitwise search finds the k-th
 //                 largest key, ties are admitted in ascending index order,
-//                 the kept indices are compacted in ascending order; the row
-//                 is then overwritten with its softmax probabilities;
+//                 the kept indices are compacted in ascending order (with
+//                 their counts below each key-chunk boundary of the fine
+//                 branch); the row is then overwritten with its softmax
+//                 probabilities;
 //   pv            c = probabilities @ pooled v, 64 rows x D per block.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -103,7 +105,9 @@ template <int MAXM>
 __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(float* __restrict__ S, int H,
                                                                   int Nt, int Ns, int P, int NV,
                                                                   int topk, float scale_log2,
-                                                                  int32_t* __restrict__ sel) {
+                                                                  int32_t* __restrict__ sel,
+                                                                  int nchunks, int chunk_tiles,
+                                                                  int32_t* __restrict__ choff) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= H * Nt) return;  // wave-uniform
@@ -142,6 +146,12 @@ __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(float* __restr
     for (int m = 0; m < MAXM; ++m) gt += (ok[m] && key[m] > thr) ? 1 : 0;
     const int need = topk - wave_sum_i(gt);  // ties to admit, lowest index first
     const uint64_t below = (uint64_t(1) << lane) - 1;
+    // Lane c <= nchunks also counts the kept ids below c * chunk_tiles (the
+    // key-chunk boundaries of the fine branch): the count before block xm
+    // plus the kept lanes of block xm below xr.
+    const int xb = min(lane * chunk_tiles, Nt);
+    const int xm = xb >> 6, xr = xb & 63;
+    int below_x = topk;
     int tie_base = 0, out_base = 0;
     int32_t* dst = sel + (static_cast<size_t>(h) * NV + (i - P)) * topk;
 #pragma unroll
@@ -153,8 +163,11 @@ __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(float* __restr
       const bool take = ok[m] && (key[m] > thr || (tie && rank < need));
       const uint64_t omask = __ballot(take);
       if (take) dst[out_base + __popcll(omask & below)] = lane + 64 * m;
+      if (m == xm) below_x = out_base + __popcll(omask & ((uint64_t(1) << xr) - 1));
       out_base += __popcll(omask);
     }
+    if (nchunks > 1 && lane <= nchunks)
+      choff[(static_cast<size_t>(h) * NV + (i - P)) * (nchunks + 1) + lane] = below_x;
   }
 
   // Softmax over all key tiles with the 1/sqrt(D) scale (log2 domain).
@@ -270,15 +283,15 @@ hipError_t launch_d(const CoarseArgs& a, hipStream_t stream) {
   dim3 g2((rows + 3) / 4);
   const int maxm = (a.Nt + 63) / 64;
   if (maxm <= 4)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<4>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<4>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
   else if (maxm <= 8)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<8>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<8>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
   else if (maxm <= 16)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<16>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<16>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
   else if (maxm <= 32)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<32>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<32>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
   else
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<64>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel);
+    hipLaunchKernelGGL((coarse_softmax_topk_kernel<64>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 

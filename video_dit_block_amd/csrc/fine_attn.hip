@@ -36,8 +36,14 @@
 //     MFMA operand reads;
 //   - partial key tiles skip their empty 16-key chunks entirely;
 //   - blocks are mapped to the 8 XCDs so that each XCD works through its own
-//     heads, head by head, prefix (long) items first: the 32 CUs of an XCD
-//     sweep the same head's K/V, which keeps it hot in that XCD's L2.
+//     heads, head by head: the 32 CUs of an XCD sweep the same head's K/V;
+//   - long key lists are cut into key chunks, one launch each: every query
+//     tile of a head visits its tiles of the current chunk at about the same
+//     time, so those reads mostly hit the L2 (and the Infinity Cache) instead
+//     of HBM.  Each wave's running state (O^T, running max, its lanes' row
+//     sums) is stored in fp32 at the end of a launch and loaded at the start
+//     of the next; visit order and arithmetic are those of a single launch,
+//     so the result is the same bit for bit.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -93,9 +99,10 @@ struct IoOps<float> {  // fp32 I/O; the MFMA operands are rounded to bf16
   }
 };
 
-// (head, query tile) of block b.  With heads divisible by 8, XCD x (blocks
-// b = x mod 8) owns heads x, x+8, ...; inside an XCD, the prefix items of its
-// heads come first, then the video items head by head.
+// (head, query tile) of block b in a single-launch forward.  With heads
+// divisible by 8, XCD x (blocks b = x mod 8) owns heads x, x+8, ...; inside
+// an XCD, the prefix items of its heads come first, then the video items
+// head by head.
 __device__ __forceinline__ void decode_item(int b, int H, int P, int NV, int& h, int& i) {
   if ((H & 7) == 0) {
     const int x = b & 7;
@@ -123,6 +130,21 @@ __device__ __forceinline__ void decode_item(int b, int H, int P, int NV, int& h,
   }
 }
 
+// (head, query tile) of block b in one key-chunk launch: XCD x works through
+// its heads x, x+8, ... one at a time, every query tile of a head in turn, so
+// the XCD's L2 only has to hold the current head's chunk of K and V.
+__device__ __forceinline__ void decode_item_chunked(int b, int H, int Nt, int& h, int& i) {
+  if ((H & 7) == 0) {
+    const int s = b >> 3;
+    const int k = s / Nt;
+    i = s - k * Nt;
+    h = (b & 7) + 8 * k;
+  } else {
+    h = b / Nt;
+    i = b - h * Nt;
+  }
+}
+
 // s_waitcnt immediate that waits for vmcnt <= N (N < 16, OR-ed in) and leaves
 // expcnt and lgkmcnt unconstrained.  The builtin, unlike inline asm, is seen
 // by the compiler's own wait-count pass, which then does not add a
@@ -137,7 +159,9 @@ __device__ __forceinline__ int swz256(int row) { return row & 15; }
 template <typename TIO, int D>
 __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
                                                           const int32_t* __restrict__ valid,
-                                                          const int32_t* __restrict__ sel) {
+                                                          const int32_t* __restrict__ sel,
+                                                          const int32_t* __restrict__ choff,
+                                                          float* __restrict__ state, int chunk) {
   constexpr int KROW = D / 8;                  // 16-byte chunks per K row
   constexpr int TILE_BYTES = 64 * D * 2;       // one K (or V^T) tile
   constexpr int LOADS = TILE_BYTES / 1024 / 2; // 1 KB DMA loads per wave per tile
@@ -154,7 +178,32 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   const int H = a.H, Nt = a.Nt, P = a.P, NV = a.NV, topk = a.topk;
 
   int hd, i;
-  decode_item(blockIdx.x, H, P, NV, hd, i);
+  if (a.nchunks > 1)
+    decode_item_chunked(blockIdx.x, H, Nt, hd, i);
+  else
+    decode_item(blockIdx.x, H, P, NV, hd, i);
+
+  // Visit list: prefix tiles 0..P-1 then the selected video tiles (all
+  // tiles for a prefix query tile), ascending.  This launch covers the part
+  // of it with ids in [chunk * chunk_tiles, (chunk + 1) * chunk_tiles).
+  const bool dense = i < P;
+  int beg = 0, end = dense ? Nt : P + topk;
+  if (a.nchunks > 1) {
+    const int lo = chunk * a.chunk_tiles;
+    const int hi = min(lo + a.chunk_tiles, Nt);
+    if (dense) {
+      beg = lo;
+      end = hi;
+    } else {
+      const int32_t* co = choff + (static_cast<size_t>(hd) * NV + (i - P)) * (a.nchunks + 1) + chunk;
+      beg = min(lo, P) + co[0];
+      end = min(hi, P) + co[1];
+    }
+  }
+  const bool first = chunk == 0;
+  const bool last = chunk == a.nchunks - 1;
+  // Nothing to add, and the running state stays where it is.
+  if (beg >= end && !first && !last) return;
 
   // Query fragment: B operand of S^T = K Q^T (column = query, k = channel).
   const TIO* q = static_cast<const TIO*>(a.q);
@@ -171,8 +220,6 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
       qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 
-  const int nlist = i < P ? Nt : P + topk;
-  const bool dense = i < P;
   const int32_t* sl = sel + (dense ? 0 : (static_cast<size_t>(hd) * NV + (i - P)) * topk);
   const char* kth = reinterpret_cast<const char*>(a.kt) + static_cast<size_t>(hd) * Nt * TILE_BYTES;
   const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nt * TILE_BYTES;
@@ -248,20 +295,47 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   const int vswz_r = swz128(l32);
 
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  // Running state of this wave's 32 rows: O^T accumulators, running max (in
+  // log2 units) and this lane's partial row sum.  Between key-chunk launches
+  // it lives in `state`, one 16-byte quad per lane per 4 words, coalesced:
+  // quads 0..4NB-1 hold oacc, quad 4NB holds (m_run, l_run, 0, 0).
   f32x16 oacc[NB];
-#pragma unroll
-  for (int n = 0; n < NB; ++n)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
   float m_run = -INFINITY;
   float l_run = 0.0f;
+  f32x4* wstate = reinterpret_cast<f32x4*>(state) +
+                  ((static_cast<size_t>(hd) * Nt + i) * 2 + w) * (4 * NB + 1) * 64 + lane;
+  if (!first && active) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const f32x4 t = __builtin_nontemporal_load(wstate + (4 * n + k4) * 64);
+        oacc[n][4 * k4 + 0] = t.x;
+        oacc[n][4 * k4 + 1] = t.y;
+        oacc[n][4 * k4 + 2] = t.z;
+        oacc[n][4 * k4 + 3] = t.w;
+      }
+    const f32x4 ml = __builtin_nontemporal_load(wstate + 4 * NB * 64);
+    m_run = ml.x;
+    l_run = ml.y;
+  } else {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
+  }
 
-  int j = tile_at(0);
-  int nj = valid[j];
-  VSA_LOAD_K(kth + static_cast<size_t>(j) * TILE_BYTES, k_loads(nj));
-  VSA_LOAD_V(vth + static_cast<size_t>(j) * TILE_BYTES, nj);
+  int j = 0, nj = 0;
+  if (beg < end) {
+    j = tile_at(beg);
+    nj = valid[j];
+    VSA_LOAD_K(kth + static_cast<size_t>(j) * TILE_BYTES, k_loads(nj));
+    VSA_LOAD_V(vth + static_cast<size_t>(j) * TILE_BYTES, nj);
+  }
+  // Query and state registers (and the first tile) have landed.
+  __builtin_amdgcn_s_waitcnt(kWaitVm);
 
-  for (int it = 0; it < nlist; ++it) {
+  for (int it = beg; it < end; ++it) {
     const int nchunk = active ? (nj + 15) >> 4 : 0;   // 16-key chunks to process
     // K(t) landed (V(t) may still be in flight).
     __builtin_amdgcn_s_waitcnt(kWaitVm | LOADS);
@@ -285,7 +359,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     VSA_BARRIER();  // every wave is done with K(t)
     // The last iteration re-requests its own tile, so that every iteration
     // issues the same loads and the wait counts below stay exact.
-    const int jn = it + 1 < nlist ? tile_at(it + 1) : j;
+    const int jn = it + 1 < end ? tile_at(it + 1) : j;
     const int njn = valid[jn];
     const int kl_next = k_loads(njn);
     VSA_LOAD_K(kth + static_cast<size_t>(jn) * TILE_BYTES, kl_next);
@@ -374,6 +448,22 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 #undef VSA_LOAD_V
 #undef VSA_BARRIER
 
+  if (!last) {
+    if (active) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const f32x4 t = {oacc[n][4 * k4 + 0], oacc[n][4 * k4 + 1], oacc[n][4 * k4 + 2],
+                           oacc[n][4 * k4 + 3]};
+          __builtin_nontemporal_store(t, wstate + (4 * n + k4) * 64);
+        }
+      const f32x4 ml = {m_run, l_run, 0.0f, 0.0f};
+      __builtin_nontemporal_store(ml, wstate + 4 * NB * 64);
+    }
+    return;
+  }
+
   // Epilogue: normalise, add gate * coarse, store at the packed row.
   l_run += __shfl_xor(l_run, 32);
   if (pr >= 0) {
@@ -404,9 +494,14 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 template <typename TIO, int D>
 hipError_t launch(const FineArgs& a, hipStream_t stream) {
   const int blocks = a.H * a.Nt;
-  hipLaunchKernelGGL((fine_attn_kernel<TIO, D>), dim3(blocks), dim3(128), 0, stream, a, a.valid,
-                     a.sel);
-  return hipGetLastError();
+  const int nchunks = a.nchunks > 1 ? a.nchunks : 1;
+  for (int c = 0; c < nchunks; ++c) {
+    hipLaunchKernelGGL((fine_attn_kernel<TIO, D>), dim3(blocks), dim3(128), 0, stream, a,
+                       a.valid, a.sel, a.choff, a.state, c);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

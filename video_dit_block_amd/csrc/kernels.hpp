@@ -22,7 +22,9 @@ struct CoarseArgs {
   float* scores;                // [H][Nt][Ns]
   float* coarse;                // [H][Nt][D]
   int32_t* sel;                 // [H][NV][topk]
+  int32_t* choff;               // [H][NV][nchunks + 1], written if nchunks > 1
   int H, Nt, Ns, P, NV, topk, D;
+  int nchunks, chunk_tiles;
 };
 hipError_t launch_coarse(const CoarseArgs& a, hipStream_t stream);
 
@@ -37,7 +39,10 @@ struct FineArgs {
   const int32_t* perm;          // [Nt][64]
   const int32_t* valid;         // [Nt]
   const int32_t* sel;           // [H][NV][topk]
+  const int32_t* choff;         // [H][NV][nchunks + 1] (nchunks > 1)
+  float* state;                 // running softmax state between chunks (nchunks > 1)
   int H, Nt, P, NV, topk, D;
+  int nchunks, chunk_tiles;
 };
 hipError_t launch_fine(const FineArgs& a, hipStream_t stream);
 

@@ -29,6 +29,71 @@ int64_t topk_rule(int64_t nv, double s) {
   return k < 1 ? 1 : k;
 }
 
+namespace {
+
+// Workspace layout; every region 256-byte aligned, sizes in 64-bit.
+void lay_out(vsa_h3_plan* plan) {
+  const uint64_t h64 = static_cast<uint64_t>(plan->heads);
+  const uint64_t d64 = static_cast<uint64_t>(plan->head_dim);
+  const uint64_t nt64 = static_cast<uint64_t>(plan->Nt);
+  const uint64_t nv64 = static_cast<uint64_t>(plan->NV);
+  const int64_t ns = (plan->Nt + 3) / 4 * 4;
+  Layout& lo = plan->layout;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    uint64_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  lo.perm = take(nt64 * kTile * 4);
+  lo.valid = take(nt64 * 4);
+  lo.kt = take(h64 * nt64 * kTile * d64 * 2);
+  lo.vt = take(h64 * nt64 * kTile * d64 * 2);
+  lo.qp = take(h64 * nt64 * d64 * 4);
+  lo.kp = take(h64 * nt64 * d64 * 4);
+  lo.vp = take(h64 * nt64 * d64 * 4);
+  lo.scores = take(h64 * nt64 * static_cast<uint64_t>(ns) * 4);
+  lo.coarse = take(h64 * nt64 * d64 * 4);
+  lo.sel = take(h64 * nv64 * static_cast<uint64_t>(plan->topk) * 4);
+  const bool chunked = plan->num_chunks > 1;
+  lo.choff = take(chunked ? h64 * nv64 * static_cast<uint64_t>(plan->num_chunks + 1) * 4 : 0);
+  // Two waves of 64 lanes per query tile.
+  lo.state = take(chunked ? h64 * nt64 * 2 * 64 *
+                                static_cast<uint64_t>(state_words_per_lane(plan->head_dim)) * 4
+                          : 0);
+  lo.total = off < 256 ? 256 : off;
+  lo.ns = ns;
+}
+
+}  // namespace
+
+vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
+  if (chunk_tiles < 0) {
+    set_error("chunk_tiles must be >= 0 (0 = automatic)");
+    return VSA_E_ARG;
+  }
+  const int64_t Nt = plan->Nt;
+  int64_t ch;
+  if (chunk_tiles == 0) {
+    // Largest chunk within kChunkBytes, then balanced over the chunks.
+    const int64_t cap = static_cast<int64_t>(kChunkBytes / (uint64_t(256) * plan->head_dim));
+    const int64_t nc = std::max<int64_t>(1, ceil_div(Nt, cap));
+    ch = std::max<int64_t>(1, ceil_div(Nt, nc));
+  } else {
+    ch = chunk_tiles;
+  }
+  const int64_t nc = Nt == 0 ? 0 : ceil_div(Nt, ch);
+  if (nc > kMaxKeyChunks) {
+    set_error("chunk_tiles " + std::to_string(ch) + " gives " + std::to_string(nc) +
+              " key chunks; at most " + std::to_string(kMaxKeyChunks) + " are supported");
+    return VSA_E_ARG;
+  }
+  plan->chunk_tiles = static_cast<int32_t>(std::min<int64_t>(ch, std::max<int64_t>(Nt, 1)));
+  plan->num_chunks = static_cast<int32_t>(nc);
+  lay_out(plan);
+  return VSA_OK;
+}
+
 vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_dims3 grid,
                       vsa_dims3 tile, int32_t heads, int32_t head_dim, double sparsity,
                       vsa_h3_plan* plan) {
@@ -157,29 +222,7 @@ vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_di
     plan->tile_slot[r] = static_cast<int32_t>(j * kTile + slot);
   }
 
-  // Workspace layout; every region 256-byte aligned, sizes in 64-bit.
-  const uint64_t h64 = static_cast<uint64_t>(heads), d64 = static_cast<uint64_t>(head_dim);
-  const uint64_t nt64 = static_cast<uint64_t>(Nt);
-  const int64_t ns = (Nt + 3) / 4 * 4;
-  Layout& lo = plan->layout;
-  uint64_t off = 0;
-  auto take = [&](uint64_t bytes) {
-    uint64_t at = off;
-    off = align256(off + bytes);
-    return at;
-  };
-  lo.perm = take(nt64 * kTile * 4);
-  lo.valid = take(nt64 * 4);
-  lo.kt = take(h64 * nt64 * kTile * d64 * 2);
-  lo.vt = take(h64 * nt64 * kTile * d64 * 2);
-  lo.qp = take(h64 * nt64 * d64 * 4);
-  lo.kp = take(h64 * nt64 * d64 * 4);
-  lo.vp = take(h64 * nt64 * d64 * 4);
-  lo.scores = take(h64 * nt64 * static_cast<uint64_t>(ns) * 4);
-  lo.coarse = take(h64 * nt64 * d64 * 4);
-  lo.sel = take(h64 * static_cast<uint64_t>(NV) * static_cast<uint64_t>(plan->topk) * 4);
-  lo.total = off < 256 ? 256 : off;
-  lo.ns = ns;
+  return set_chunk_tiles(plan, 0);
   return VSA_OK;
 }
 

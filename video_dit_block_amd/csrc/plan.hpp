@@ -13,11 +13,24 @@ namespace vsa {
 
 constexpr int kTile = 64;          // tokens per tile (video (4,4,4) and prefix)
 constexpr int kMaxTilesCoarse = 4096;  // key tiles one wave can hold in the coarse/top-k kernel
+constexpr int kMaxKeyChunks = 63;      // chunk boundaries one wave writes per query tile
+// K+V bytes of one head's key chunk in the fine branch.  All query tiles of a
+// head sweep a chunk together, so the eight XCDs' current chunks (8 x 10 MiB)
+// stay in the 256 MiB Infinity Cache and much of the reuse among the blocks
+// of one XCD hits its 4 MiB L2.  Smaller chunks raise the L2 hit rate but pass
+// the running state through memory more often; at the 73,600-token layouts,
+// 128- to 320-tile chunks measured alike on random selections and larger
+// chunks did better on spatially smooth ones.
+constexpr uint64_t kChunkBytes = uint64_t(10) << 20;
 
 struct Layout {
-  uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, total;
+  uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, total;
   int64_t ns;  // scores row stride
 };
+
+// fp32 words of fine-branch state per wave lane (O accumulators + running
+// max + running sum, padded to 4): head_dim / 2 + 4.
+inline int state_words_per_lane(int head_dim) { return head_dim / 2 + 4; }
 
 }  // namespace vsa
 
@@ -29,6 +42,8 @@ struct vsa_h3_plan {
   std::vector<int32_t> perm;       // [Nt*64]
   std::vector<int32_t> valid;      // [Nt]
   std::vector<int32_t> tile_slot;  // [L]
+  int32_t chunk_tiles = 0;         // key tiles per fine-branch chunk
+  int32_t num_chunks = 0;          // ceil(Nt / chunk_tiles); 0 when Nt == 0
   vsa::Layout layout{};
 };
 
@@ -41,6 +56,10 @@ const char* get_error();
 int64_t topk_rule(int64_t num_video_tiles, double sparsity);
 
 // Builds the plan; returns VSA_OK or an error status (message set).
+// Sets the key-chunk size of the fine branch (0 = automatic) and lays out
+// the workspace again.
+vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles);
+
 vsa_status build_plan(const int64_t* token_tags, const int64_t* position_ids, int64_t L,
                       vsa_dims3 grid, vsa_dims3 tile, int32_t heads, int32_t head_dim,
                       double sparsity, vsa_h3_plan* plan);
