@@ -52,6 +52,27 @@ design notes of the repository):
   R13 all non-video tokens precede all video tokens; video positions are
      zero-based and cover the grid exactly once.
 
+Optional upstream step, fused into the tile gather ("FastH3 NVFP4 on RTX PRO
+6000", section "Model integration": QK-norm and RoPE are applied to the
+tile-ordered q and k with cos/sin tables computed once per step, and pad rows
+stay zero through them).  The pages give neither the H3 norm weights nor the
+RoPE frequencies, so both arrive as inputs:
+  R14 QK-norm is an RMS norm over head_dim for every (token, head), with one
+     fp32 weight vector [D] for q and one for k, shared by all heads; eps is
+     added to the mean square;
+  R15 canonical fp32 order (so that pooled values and the selection stay
+     reproducible bit for bit): ss = +0, then ss = ss + x_d * x_d for
+     d = 0..D-1 (separately rounded, no fused multiply-add);
+     inv = 1 / sqrt(ss / D + eps), each of the division, addition, square
+     root and reciprocal correctly rounded; y_d = (x_d * inv) * w_d;
+  R16 RoPE rotates the interleaved pairs (y_2i, y_2i+1), i = 0..D/2-1, by the
+     caller's per-token cos/sin [L, D/2] as the complex product
+     (a + ib)(c + is): a' = a*c - b*s, b' = a*s + b*c, products and sums
+     separately rounded in fp32;
+  R17 the normalised, rotated q and k are rounded to the I/O dtype (bf16
+     nearest-even, or kept fp32) and are then the attention inputs: the
+     pooling, scores, selection and fine branch all use them; v is unchanged.
+
 Pins (tests/test_oracle_pins.py) -- each function is checked against
 something other than itself:
   topk_count         closed-form values and the double-evaluation case
@@ -68,6 +89,12 @@ something other than itself:
                      all-equal pooled keys -> mean of pooled values
   combine            gate 0 -> out == o; tile-constant inputs, gate 1 ->
                      out == 2 * dense; per-channel gates
+  qk_norm_rope       a hand-computed 2-channel row; exact invariance under
+                     power-of-two scaling (eps 0); unit RMS with unit
+                     weights; identity and quarter-turn tables; one pair
+                     against Python complex multiplication; rotation keeps
+                     pair norms; dot products depend only on the position
+                     difference
 No function here is marked "parity unpinned"; the numeric values of a real
 FastH3 forward are not printed anywhere on the pages, so parity rests on the
 pins above.
@@ -294,6 +321,32 @@ def combine(o: np.ndarray, g: np.ndarray, c: np.ndarray, geom: Geometry) -> np.n
     return o + g.astype(np.float64) * c[tile]
 
 
+def qk_norm_rope(x32: np.ndarray, weight: np.ndarray, eps: float, cos: np.ndarray,
+                 sin: np.ndarray) -> np.ndarray:
+    """RMS norm over the last axis, then RoPE on interleaved pairs, in the
+    canonical fp32 order of R14-R16.  x32 [L, D] fp32 (one head), weight [D],
+    cos / sin [L, D/2] fp32.  Returns [L, D] fp32 (before the R17 rounding)."""
+    x = np.asarray(x32, dtype=np.float32)
+    L, D = x.shape
+    f32 = np.float32
+    ss = np.zeros(L, dtype=f32)
+    for d in range(D):
+        ss = np.add(ss, np.multiply(x[:, d], x[:, d], dtype=f32), dtype=f32)
+    ms = np.divide(ss, f32(D), dtype=f32)
+    r = np.sqrt(np.add(ms, f32(eps), dtype=f32), dtype=f32)
+    inv = np.divide(f32(1.0), r, dtype=f32)
+    y = np.multiply(np.multiply(x, inv[:, None], dtype=f32),
+                    np.asarray(weight, dtype=f32)[None, :], dtype=f32)
+    a, b = y[:, 0::2], y[:, 1::2]
+    c = np.asarray(cos, dtype=f32)
+    s = np.asarray(sin, dtype=f32)
+    out = np.empty_like(y)
+    out[:, 0::2] = np.subtract(np.multiply(a, c, dtype=f32), np.multiply(b, s, dtype=f32),
+                               dtype=f32)
+    out[:, 1::2] = np.add(np.multiply(a, s, dtype=f32), np.multiply(b, c, dtype=f32), dtype=f32)
+    return out
+
+
 def round_bf16_from_f64(x: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bfloat16 (ties to even), returned as
     float64.  One rounding step, straight from float64."""
@@ -339,6 +392,23 @@ def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
                  geom, sel, scale, items)
         out = combine(o, to_f32(gate[:, h, :]), c, geom)
     return HeadResult(qp, kp, vp, S, sel, c, o, out)
+
+
+def prep_qk(q, k, q_weight, k_weight, eps, cos, sin):
+    """R14-R17 on every head: returns the attention inputs (q', k') as float32
+    arrays [L, H, D] holding bf16 values when q is bf16 (else fp32 values)."""
+    qa = to_f32(q)
+    ka = to_f32(k)
+    is_bf16 = str(getattr(q, "dtype", "")).endswith("bfloat16")
+    outs = []
+    for x, wgt in ((qa, q_weight), (ka, k_weight)):
+        y = np.empty_like(x)
+        for h in range(x.shape[1]):
+            r = qk_norm_rope(x[:, h, :], wgt, eps, cos, sin)
+            y[:, h, :] = (round_bf16_from_f64(r.astype(np.float64)).astype(np.float32)
+                          if is_bf16 else r)
+        outs.append(y)
+    return outs[0], outs[1]
 
 
 def forward(q, k, v, gate, token_tags, position_ids, grid, sparsity, tile=TILE_DIMS,

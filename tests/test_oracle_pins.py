@@ -445,3 +445,114 @@ def test_combine_with_independent_branches():
     out = O.combine(r.o, gate, r.c, g)
     assert np.max(np.abs(o_ref - c_ref[tile])) > 1e-2            # o and c really differ
     assert np.max(np.abs(out - (o_ref + gate * c_ref[tile]))) < 1e-5
+
+
+# ----------------------------------------------------------------- QK-norm + RoPE (optional upstream step)
+def _ident_tables(L, D):
+    return np.ones((L, D // 2), np.float32), np.zeros((L, D // 2), np.float32)
+
+
+def test_qk_norm_hand_computed_row():
+    # x = (3, 4), unit weights, eps 0: mean square 12.5, y = x / sqrt(12.5)
+    x = np.array([[3.0, 4.0]], np.float32)
+    c, s = _ident_tables(1, 2)
+    y = oracle.qk_norm_rope(x, np.ones(2, np.float32), 0.0, c, s)
+    want = np.array([3.0, 4.0]) / math.sqrt(12.5)
+    assert np.allclose(y[0].astype(np.float64), want, rtol=3e-7, atol=0)
+    # the weight scales each channel afterwards
+    y2 = oracle.qk_norm_rope(x, np.array([2.0, 0.5], np.float32), 0.0, c, s)
+    assert np.allclose(y2[0].astype(np.float64), want * [2.0, 0.5], rtol=3e-7, atol=0)
+
+
+def test_qk_norm_power_of_two_scale_invariance_exact():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((50, 64)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, 64).astype(np.float32)
+    c, s = _ident_tables(50, 64)
+    base = oracle.qk_norm_rope(x, w, 0.0, c, s)
+    for k in (-6, -1, 3, 10):
+        assert np.array_equal(oracle.qk_norm_rope(x * np.float32(2.0 ** k), w, 0.0, c, s), base)
+
+
+def test_qk_norm_unit_rms_with_unit_weights():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((40, 128)) * rng.uniform(0.1, 30, (40, 1))).astype(np.float32)
+    c, s = _ident_tables(40, 128)
+    y = oracle.qk_norm_rope(x, np.ones(128, np.float32), 0.0, c, s).astype(np.float64)
+    assert np.allclose(np.sqrt((y ** 2).mean(axis=1)), 1.0, rtol=2e-6, atol=0)
+    # eps shrinks a small row toward zero exactly as 1/sqrt(ms + eps) says
+    tiny = np.full((1, 4), 1e-3, np.float32)
+    y = oracle.qk_norm_rope(tiny, np.ones(4, np.float32), 1e-6, *_ident_tables(1, 4))
+    assert np.allclose(y[0], 1e-3 / math.sqrt(1e-6 + 1e-6), rtol=1e-6)
+
+
+def test_rope_identity_and_quarter_turn():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((8, 16)).astype(np.float32)
+    w = np.ones(16, np.float32)
+    c, s = _ident_tables(8, 16)
+    y = oracle.qk_norm_rope(x, w, 0.0, c, s)
+    # a quarter turn maps each pair (a, b) to (-b, a) exactly
+    q = oracle.qk_norm_rope(x, w, 0.0, np.zeros_like(c), np.ones_like(s))
+    assert np.array_equal(q[:, 0::2], -y[:, 1::2]) and np.array_equal(q[:, 1::2], y[:, 0::2])
+
+
+def test_rope_pair_is_complex_multiplication():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((6, 8)).astype(np.float32)
+    w = np.ones(8, np.float32)
+    theta = rng.uniform(-math.pi, math.pi, (6, 4))
+    c, s = np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+    base = oracle.qk_norm_rope(x, w, 0.0, *_ident_tables(6, 8)).astype(np.float64)
+    y = oracle.qk_norm_rope(x, w, 0.0, c, s).astype(np.float64)
+    for r in range(6):
+        for i in range(4):
+            z = complex(base[r, 2 * i], base[r, 2 * i + 1]) * complex(float(c[r, i]), float(s[r, i]))
+            assert abs(y[r, 2 * i] - z.real) <= 4e-7 * (abs(z) + 1e-30)
+            assert abs(y[r, 2 * i + 1] - z.imag) <= 4e-7 * (abs(z) + 1e-30)
+        # rotation keeps every pair's length
+        n0 = np.hypot(base[r, 0::2], base[r, 1::2])
+        n1 = np.hypot(y[r, 0::2], y[r, 1::2])
+        assert np.allclose(n0, n1, rtol=1e-6)
+
+
+def test_rope_scores_depend_only_on_position_difference():
+    # q and k rotated by angles p*f and p'*f: q'.k' equals q rotated by (p - p')*f against k
+    rng = np.random.default_rng(4)
+    D = 32
+    freqs = 1.0 / (10000.0 ** (np.arange(D // 2) * 2.0 / D))
+    q = rng.standard_normal((1, D)).astype(np.float32)
+    k = rng.standard_normal((1, D)).astype(np.float32)
+    w = np.ones(D, np.float32)
+
+    def rot(x, p):
+        ang = (p * freqs)[None, :]
+        return oracle.qk_norm_rope(x, w, 0.0, np.cos(ang).astype(np.float32),
+                                   np.sin(ang).astype(np.float32)).astype(np.float64)
+    for p, pp in ((7, 3), (40, 2), (5, 5), (0, 11)):
+        lhs = float(rot(q, p) @ rot(k, pp).T)
+        rhs = float(rot(q, p - pp) @ rot(k, 0).T)
+        assert abs(lhs - rhs) < 2e-5 * D
+
+
+def test_rope_rotates_adjacent_channel_pairs_of_the_input():
+    # identity tables give the normalised input in its own channel order
+    # (float64 formula), and a table that turns only pair i changes only
+    # input channels 2i and 2i+1
+    rng = np.random.default_rng(5)
+    D = 16
+    x = rng.standard_normal((3, D)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    c, s = _ident_tables(3, D)
+    y = oracle.qk_norm_rope(x, w, 1e-6, c, s).astype(np.float64)
+    x64 = x.astype(np.float64)
+    ref = x64 / np.sqrt((x64 ** 2).mean(axis=1, keepdims=True) + 1e-6) * w
+    assert np.allclose(y, ref, rtol=1e-6, atol=0)
+    for i in (0, 3, 7):
+        c2, s2 = c.copy(), s.copy()
+        c2[:, i], s2[:, i] = 0.0, 1.0
+        z = oracle.qk_norm_rope(x, w, 1e-6, c2, s2).astype(np.float64)
+        other = [d for d in range(D) if d not in (2 * i, 2 * i + 1)]
+        assert np.array_equal(z[:, other], y[:, other])
+        assert np.array_equal(z[:, 2 * i], -y[:, 2 * i + 1])
+        assert np.array_equal(z[:, 2 * i + 1], y[:, 2 * i])

@@ -180,3 +180,30 @@ def make_inputs(w: Workload, seed: int = 0, video_order: str = "raster"):
     out["token_tags"] = tags
     out["position_ids"] = pos
     return out
+
+
+def make_qk_prep_inputs(w: Workload, position_ids, seed: int = 0, theta: float = 10000.0):
+    """Synthetic inputs of the optional QK-norm + RoPE step (the H3 weights and
+    frequencies are not published): norm weights for q and k drawn from
+    U(0.5, 1.5), eps 1e-6, and per-token cos/sin tables [L, D/2] of a 3D RoPE
+    whose pairs are split over (t, y, x) as (D/2 - 2*(D/6), D/6, D/6) with
+    frequencies theta^(-j/n) inside each axis; prefix tokens get angle 0.
+    Returns dict(q_weight, k_weight, eps, cos, sin) of CPU float32 tensors."""
+    D = w.head_dim
+    g = torch.Generator().manual_seed(seed + 7919)
+    qw = torch.rand(D, generator=g, dtype=torch.float32) + 0.5
+    kw = torch.rand(D, generator=g, dtype=torch.float32) + 0.5
+    pairs = D // 2
+    ny = nx = D // 6
+    nt = pairs - ny - nx
+    pos = torch.as_tensor(position_ids, dtype=torch.float64).reshape(-1, 3)
+    L = pos.shape[0]
+    ang = torch.zeros((L, pairs), dtype=torch.float64)
+    start = 0
+    n_pre = w.n_prefix_tokens
+    for axis, n in enumerate((nt, ny, nx)):
+        freqs = theta ** (-torch.arange(n, dtype=torch.float64) / max(n, 1))
+        ang[n_pre:, start:start + n] = pos[n_pre:, axis:axis + 1] * freqs[None, :]
+        start += n
+    return {"q_weight": qw, "k_weight": kw, "eps": 1e-6,
+            "cos": torch.cos(ang).to(torch.float32), "sin": torch.sin(ang).to(torch.float32)}
