@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="768p10s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qk-prep", action="store_true",
+                    help="time the forward with QK RMS norm + RoPE fused into the gather "
+                         "(synthetic weights and cos/sin tables)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="counter runs: one 1 GiB device copy (traffic calibration), then the "
                          "warmup and timed forwards; no CPU baseline")
@@ -164,7 +167,7 @@ def main():
     import torch
     sys.path.insert(0, ROOT)
     import video_dit_block_amd as vsa
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS, make_inputs, make_qk_prep_inputs
 
     w = WORKLOADS[args.workload]
     log(f"bench: workload {w.name}: {w.description}")
@@ -174,7 +177,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     xd = {n: x[n].to(dev) for n in ("q", "k", "v", "gate")}
-    plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim, w.sparsity)
+    plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim, w.sparsity,
+                    qk_prep=args.qk_prep)
     stream = torch.cuda.current_stream(dev)
     ws = plan.workspace(dev, stream.cuda_stream)
     out = torch.empty_like(xd["q"])
@@ -194,9 +198,21 @@ def main():
     hip = HipEvents()
     evs = [hip.create(4) for _ in range(args.steps)]
 
+    if args.qk_prep:
+        prep = make_qk_prep_inputs(w, x["position_ids"])
+        pd = {n: prep[n].to(dev) for n in ("q_weight", "k_weight", "cos", "sin")}
+
     def step(events=None):
-        vsa.vsa_h3_forward_timed(plan.handle, *ptrs, io, out.data_ptr(), sel.data_ptr(),
-                                 ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream, events)
+        if args.qk_prep:
+            vsa.vsa_h3_forward_qk_prep(plan.handle, *ptrs, pd["q_weight"].data_ptr(),
+                                       pd["k_weight"].data_ptr(), prep["eps"],
+                                       pd["cos"].data_ptr(), pd["sin"].data_ptr(), io,
+                                       out.data_ptr(), sel.data_ptr(), ws.data_ptr(),
+                                       plan.workspace_bytes, stream.cuda_stream, events)
+        else:
+            vsa.vsa_h3_forward_timed(plan.handle, *ptrs, io, out.data_ptr(), sel.data_ptr(),
+                                     ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream,
+                                     events)
 
     for _ in range(args.warmup):
         step()
@@ -245,6 +261,7 @@ def main():
             "workload": w.name, "tokens": plan.L, "heads": w.heads, "head_dim": w.head_dim,
             "prefix_tokens": w.n_prefix_tokens, "grid": list(w.grid),
             "sparsity": w.sparsity, "topk": plan.topk, "tiles": plan.num_tiles,
+            "qk_prep": bool(args.qk_prep),
             "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
             "flops_effective": total, "flops_fine_padded_tiles": padded_fine,
             "stage_ms": {"permute_pool": round(float(stage[:, 0].mean()), 4),
@@ -263,7 +280,7 @@ def main():
             "avg_launch_ms": round(fine_ms / launches, 4),
         },
     }
-    if not args.no_cpu_baseline and not args.profile_pass:
+    if not args.no_cpu_baseline and not args.profile_pass and not args.qk_prep:
         log("bench: timing the CPU oracle on one head (bounded sample)")
         cb, parity = cpu_baseline(x, w, out, sel_h, plan)
         rec["cpu_baseline"] = cb

@@ -92,6 +92,8 @@ typedef struct {
                               counts the selected tiles of the row with id < c * chunk_tiles */
   uint64_t state;   /* fp32 fine-branch state between key chunks (only if num_chunks > 1);
                        internal layout */
+  uint64_t qt;      /* bf16 [H][Nt][64][D]: q after QK-norm + RoPE, tile order, pad rows zero
+                       (only with vsa_h3_plan_set_qk_prep) */
 } vsa_h3_ws_layout;
 
 /* Top-k rule of VSA-H3 evaluated in IEEE double as written; 0 when
@@ -189,6 +191,43 @@ vsa_status vsa_h3_forward_oneshot(const void* q, const void* k, const void* v, c
                                   double sparsity, vsa_dims3 tile, vsa_dtype io_dtype, void* out,
                                   int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
                                   void* stream);
+
+/* Optional upstream step fused into the tile gather: QK RMS norm and RoPE
+ * (FastH3 NVFP4 on RTX PRO 6000, "Model integration": QK-norm and RoPE are
+ * applied to the tile-ordered q and k with cos/sin tables computed once per
+ * step; pad rows stay zero).  The H3 norm weights and RoPE frequencies are
+ * not published, so both are inputs.
+ *
+ * vsa_h3_plan_set_qk_prep(plan, 1) adds the workspace region that holds the
+ * normalised, rotated q in tile order (the workspace size changes: call it
+ * before sizing and uploading a workspace); 0 removes it.
+ *
+ * vsa_h3_forward_qk_prep runs the forward of vsa_h3_forward_timed on
+ *   q' = rope(norm(q, q_norm_weight)),  k' = rope(norm(k, k_norm_weight)),
+ * where, per (token, head) row x of head_dim D, in fp32 and in this order
+ * (each operation separately rounded, no fused multiply-add):
+ *   ss = sum_{d=0..D-1} x_d * x_d (sequential from +0);
+ *   inv = 1 / sqrt(ss / D + eps)  (division, square root, reciprocal
+ *         correctly rounded);
+ *   y_d = (x_d * inv) * w_d;
+ *   (y_2i, y_2i+1) -> (y_2i * c - y_2i+1 * s, y_2i * s + y_2i+1 * c) with
+ *         c = rope_cos[token][i], s = rope_sin[token][i];
+ * then rounded to io_dtype.  q', k' replace q, k everywhere (pooling,
+ * scores, selection, fine branch); v and gate are used as given.
+ *   q_norm_weight, k_norm_weight  device fp32 [head_dim], shared by all heads.
+ *   eps                           finite, >= 0.
+ *   rope_cos, rope_sin            device fp32 [L][head_dim/2], packed token order.
+ *   events                        as for vsa_h3_forward_timed (may be NULL).
+ * Errors: as vsa_h3_forward_timed; VSA_E_ARG if the plan has no QK-prep
+ * region, a table or weight pointer is NULL or not 4-byte aligned, or eps
+ * is negative or not finite. */
+vsa_status vsa_h3_plan_set_qk_prep(vsa_h3_plan* plan, int32_t enable);
+vsa_status vsa_h3_forward_qk_prep(const vsa_h3_plan* plan, const void* q, const void* k,
+                                  const void* v, const void* gate, const float* q_norm_weight,
+                                  const float* k_norm_weight, float eps, const float* rope_cos,
+                                  const float* rope_sin, vsa_dtype io_dtype, void* out,
+                                  int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
+                                  void* stream, void* const* events);
 
 void vsa_h3_plan_destroy(vsa_h3_plan* plan);
 const char* vsa_h3_last_error(void);

@@ -44,6 +44,28 @@ def run(x, grid, sparsity, dev="cuda", plan=None):
     return out, sel, plan, ws
 
 
+def run_qk_prep(x, prep, grid, sparsity, dev="cuda", plan=None, chunk_tiles=0):
+    """GPU forward with QK-norm + RoPE through the C ABI.  Returns (out, sel, plan, ws)."""
+    xd = {k: x[k].to(dev) for k in ("q", "k", "v", "gate")}
+    pd = {k: prep[k].to(dev) for k in ("q_weight", "k_weight", "cos", "sin")}
+    L, H, D = xd["q"].shape
+    if plan is None:
+        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity,
+                        chunk_tiles=chunk_tiles, qk_prep=True)
+    out, sel = vsa.forward_qk_prep(xd["q"], xd["k"], xd["v"], xd["gate"], pd["q_weight"],
+                                   pd["k_weight"], prep["eps"], pd["cos"], pd["sin"], plan=plan,
+                                   return_sel=True)
+    torch.cuda.synchronize()
+    ws = plan.workspace(xd["q"].device)
+    return out, sel, plan, ws
+
+
+def oracle_prep(x, prep):
+    """The oracle's attention inputs q', k' (float32 numpy [L, H, D])."""
+    return oracle.prep_qk(x["q"], x["k"], prep["q_weight"].numpy(), prep["k_weight"].numpy(),
+                          prep["eps"], prep["cos"].numpy(), prep["sin"].numpy())
+
+
 def intermediates(plan, ws):
     H, D, Nt = plan.heads, plan.head_dim, plan.num_tiles
     ns = plan.layout.scores_row_stride

@@ -248,3 +248,40 @@ def test_python_forward_refuses_cpu_tensors():
     x = torch.zeros((w.L, w.heads, w.head_dim))
     with pytest.raises(vsa.VsaError):
         vsa.forward(x, x, x, x, tags, pos, w.grid, w.sparsity)
+
+
+def test_qk_prep_plan_region_and_argument_errors():
+    w = WORKLOADS["tiny"]
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    base = p.workspace_bytes
+    L = _abi.lib()
+    fake = 1 << 40   # never dereferenced: every call below fails its checks first
+    args = [fake, fake + (1 << 30), fake + (2 << 30), fake + (3 << 30)]
+    tabs = [fake + (4 << 30), fake + (5 << 30), fake + (6 << 30), fake + (7 << 30)]
+    # no QK-prep region in the plan
+    assert L.vsa_h3_forward_qk_prep(p.handle, *args, tabs[0], tabs[1], 1e-6, tabs[2], tabs[3], 0,
+                                    fake + (8 << 30), None, fake + (9 << 30), base, None,
+                                    None) == _abi.VSA_E_ARG
+    p2 = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity, qk_prep=True)
+    Nt, D, H = p2.num_tiles, w.head_dim, w.heads
+    assert p2.workspace_bytes >= base + H * Nt * 64 * D * 2
+    lo = p2.layout
+    assert lo.qt % 256 == 0 and lo.qt + H * Nt * 64 * D * 2 <= lo.total
+    ws = fake + (9 << 30)
+    n = p2.workspace_bytes
+    assert L.vsa_h3_forward_qk_prep(p2.handle, *args, None, tabs[1], 1e-6, tabs[2], tabs[3], 0,
+                                    fake + (8 << 30), None, ws, n, None, None) == _abi.VSA_E_ARG
+    assert L.vsa_h3_forward_qk_prep(p2.handle, *args, tabs[0], tabs[1], -1.0, tabs[2], tabs[3], 0,
+                                    fake + (8 << 30), None, ws, n, None, None) == _abi.VSA_E_ARG
+    assert L.vsa_h3_forward_qk_prep(p2.handle, *args, tabs[0], tabs[1], float("nan"), tabs[2],
+                                    tabs[3], 0, fake + (8 << 30), None, ws, n, None,
+                                    None) == _abi.VSA_E_ARG
+    assert L.vsa_h3_forward_qk_prep(p2.handle, *args, tabs[0] + 2, tabs[1], 1e-6, tabs[2],
+                                    tabs[3], 0, fake + (8 << 30), None, ws, n, None,
+                                    None) == _abi.VSA_E_ARG
+    assert L.vsa_h3_forward_qk_prep(p2.handle, *args, tabs[0], tabs[1], 1e-6, tabs[2], tabs[3], 0,
+                                    fake + (8 << 30), None, ws, n - 1, None,
+                                    None) == _abi.VSA_E_WORKSPACE
+    vsa.vsa_h3_plan_set_qk_prep(p2.handle, False)
+    assert vsa.vsa_h3_plan_info(p2.handle).workspace_bytes == base

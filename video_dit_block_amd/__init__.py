@@ -26,10 +26,11 @@ from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
     vsa_h3_last_error,
     vsa_h3_oneshot_workspace_bytes, vsa_h3_plan_create, vsa_h3_plan_destroy, vsa_h3_plan_info,
     vsa_h3_plan_layout, vsa_h3_plan_set_chunk_tiles, vsa_h3_plan_tables, vsa_h3_plan_upload,
-    vsa_h3_topk, vsa_h3_version,
+    vsa_h3_topk, vsa_h3_version, vsa_h3_plan_set_qk_prep, vsa_h3_forward_qk_prep,
 )
 
-__all__ = ["Plan", "forward", "VsaError", "vsa_h3_topk", "vsa_h3_version"] + list(EXPORTED)
+__all__ = ["Plan", "forward", "forward_qk_prep", "VsaError", "vsa_h3_topk",
+           "vsa_h3_version"] + list(EXPORTED)
 
 
 def _host_i64(x) -> np.ndarray:
@@ -46,7 +47,7 @@ class Plan:
     """Tile geometry for one packed layout (host), plus per-device workspaces."""
 
     def __init__(self, token_tags, position_ids, grid, heads, head_dim, sparsity,
-                 tile=(4, 4, 4), chunk_tiles: int = 0):
+                 tile=(4, 4, 4), chunk_tiles: int = 0, qk_prep: bool = False):
         self.token_tags = _host_i64(token_tags).reshape(-1)
         self.position_ids = _host_i64(position_ids).reshape(-1, 3)
         self.grid = tuple(int(g) for g in grid)
@@ -56,6 +57,9 @@ class Plan:
                                          self.tile, heads, head_dim, sparsity)
         if chunk_tiles:
             vsa_h3_plan_set_chunk_tiles(self.handle, chunk_tiles)
+        if qk_prep:
+            vsa_h3_plan_set_qk_prep(self.handle, True)
+        self.qk_prep = bool(qk_prep)
         self.info = vsa_h3_plan_info(self.handle)
         self.layout = vsa_h3_plan_layout(self.handle)
         self._ws = {}
@@ -125,18 +129,20 @@ _plans: "OrderedDict[tuple, Plan]" = OrderedDict()
 _plans_lock = threading.Lock()
 
 
-def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4, 4, 4)) -> Plan:
+def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4, 4, 4),
+             qk_prep: bool = False) -> Plan:
     """Cached Plan for this exact layout (keyed by a digest of tags and positions)."""
     tags = _host_i64(token_tags).reshape(-1)
     pos = _host_i64(position_ids).reshape(-1, 3)
     digest = hashlib.sha256(tags.tobytes() + b"|" + pos.tobytes()).hexdigest()
-    key = (digest, tuple(grid), tuple(tile), int(heads), int(head_dim), float(sparsity))
+    key = (digest, tuple(grid), tuple(tile), int(heads), int(head_dim), float(sparsity),
+           bool(qk_prep))
     with _plans_lock:
         p = _plans.get(key)
         if p is not None:
             _plans.move_to_end(key)
             return p
-    p = Plan(tags, pos, grid, heads, head_dim, sparsity, tile)
+    p = Plan(tags, pos, grid, heads, head_dim, sparsity, tile, qk_prep=qk_prep)
     with _plans_lock:
         _plans[key] = p
         while len(_plans) > 8:
@@ -181,4 +187,55 @@ def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsi
     vsa_h3_forward(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), io,
                    out.data_ptr(), sel.data_ptr() if sel is not None and sel.numel() else None,
                    ws.data_ptr(), plan.workspace_bytes, stream)
+    return (out, sel) if return_sel else out
+
+
+def forward_qk_prep(q, k, v, gate, q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin,
+                    token_tags=None, position_ids=None, grid=None, sparsity=None,
+                    tile=(4, 4, 4), *, plan: Plan | None = None, out=None,
+                    return_sel: bool = False):
+    """VSA-H3 forward with QK RMS norm and RoPE applied to q and k while they
+    are gathered into tile order.  q, k, v, gate as for ``forward`` (q and k
+    before the norm); q_norm_weight, k_norm_weight: float32 CUDA [head_dim];
+    rope_cos, rope_sin: float32 CUDA [L, head_dim // 2] in packed order."""
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and gate.is_cuda):
+        raise VsaError(-1, "q, k, v and gate must be GPU tensors (there is no CPU path)")
+    if not (q.shape == k.shape == v.shape == gate.shape) or q.dim() != 3:
+        raise VsaError(-1, "q, k, v and gate must share one [L, heads, head_dim] shape")
+    if not (q.dtype == k.dtype == v.dtype == gate.dtype):
+        raise VsaError(-1, "q, k, v and gate must share one dtype")
+    io = VSA_BF16 if q.dtype == torch.bfloat16 else (VSA_F32 if q.dtype == torch.float32 else None)
+    if io is None:
+        raise VsaError(-1, f"unsupported dtype {q.dtype}")
+    L, H, D = q.shape
+    for name, t, shape in (("q_norm_weight", q_norm_weight, (D,)),
+                           ("k_norm_weight", k_norm_weight, (D,)),
+                           ("rope_cos", rope_cos, (L, D // 2)), ("rope_sin", rope_sin, (L, D // 2))):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()
+                and tuple(t.shape) == shape):
+            raise VsaError(-1, f"{name} must be a contiguous float32 GPU tensor of shape {shape}")
+    for t in (q, k, v, gate):
+        if not t.is_contiguous():
+            raise VsaError(-1, "tensors must be contiguous")
+    if plan is None:
+        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile, qk_prep=True)
+    if not plan.qk_prep:
+        raise VsaError(-1, "plan was built without qk_prep=True")
+    if (plan.L, plan.heads, plan.head_dim) != (L, H, D):
+        raise VsaError(-1, "plan does not match the tensors' [L, heads, head_dim]")
+    dev = q.device
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = plan.workspace(dev, stream)
+    if out is None:
+        out = torch.empty_like(q)
+    sel = None
+    if return_sel:
+        sel = torch.empty((H, plan.num_video_tiles, plan.topk), dtype=torch.int32, device=dev)
+    vsa_h3_forward_qk_prep(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           gate.data_ptr(), q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+                           float(eps), rope_cos.data_ptr(), rope_sin.data_ptr(), io,
+                           out.data_ptr(),
+                           sel.data_ptr() if sel is not None and sel.numel() else None,
+                           ws.data_ptr(), plan.workspace_bytes, stream)
     return (out, sel) if return_sel else out

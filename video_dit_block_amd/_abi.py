@@ -25,7 +25,7 @@ EXPORTED = (
     "vsa_h3_plan_layout",
     "vsa_h3_plan_tables", "vsa_h3_plan_upload", "vsa_h3_forward", "vsa_h3_forward_timed",
     "vsa_h3_oneshot_workspace_bytes", "vsa_h3_forward_oneshot", "vsa_h3_plan_destroy",
-    "vsa_h3_last_error", "vsa_h3_version",
+    "vsa_h3_last_error", "vsa_h3_version", "vsa_h3_plan_set_qk_prep", "vsa_h3_forward_qk_prep",
 )
 
 
@@ -51,7 +51,7 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("perm", "valid", "kt", "vt", "qp", "kp", "vp",
                                                "scores", "coarse", "sel", "total")] + \
                [("scores_row_stride", ctypes.c_int64), ("chunk_offsets", ctypes.c_uint64),
-                ("state", ctypes.c_uint64)]
+                ("state", ctypes.c_uint64), ("qt", ctypes.c_uint64)]
 
 
 _lib = None
@@ -95,6 +95,10 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_int32, ctypes.c_int32, Dims3,
                                              ctypes.c_double, Dims3, ctypes.c_int, _P, _P, _P,
                                              ctypes.c_uint64, _P]
+        L.vsa_h3_plan_set_qk_prep.argtypes = [_P, ctypes.c_int32]
+        L.vsa_h3_forward_qk_prep.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                             ctypes.c_int, _P, _P, _P, ctypes.c_uint64, _P,
+                                             ctypes.POINTER(_P)]
         L.vsa_h3_plan_destroy.argtypes = [_P]
         L.vsa_h3_plan_destroy.restype = None
         L.vsa_h3_last_error.restype = ctypes.c_char_p
@@ -183,6 +187,22 @@ def vsa_h3_forward_timed(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr
     arr = (_P * 4)(*events) if events is not None else None
     check(lib().vsa_h3_forward_timed(plan, q_ptr, k_ptr, v_ptr, gate_ptr, io_dtype, out_ptr,
                                      sel_ptr, workspace_ptr, workspace_bytes, stream, arr))
+
+
+def vsa_h3_plan_set_qk_prep(plan: int, enable: bool) -> None:
+    check(lib().vsa_h3_plan_set_qk_prep(plan, 1 if enable else 0))
+
+
+def vsa_h3_forward_qk_prep(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr: int,
+                           q_norm_weight_ptr: int, k_norm_weight_ptr: int, eps: float,
+                           rope_cos_ptr: int, rope_sin_ptr: int, io_dtype: int, out_ptr: int,
+                           sel_ptr, workspace_ptr: int, workspace_bytes: int, stream: int,
+                           events=None) -> None:
+    arr = (_P * 4)(*events) if events is not None else None
+    check(lib().vsa_h3_forward_qk_prep(plan, q_ptr, k_ptr, v_ptr, gate_ptr, q_norm_weight_ptr,
+                                       k_norm_weight_ptr, float(eps), rope_cos_ptr, rope_sin_ptr,
+                                       io_dtype, out_ptr, sel_ptr, workspace_ptr,
+                                       workspace_bytes, stream, arr))
 
 
 def vsa_h3_oneshot_workspace_bytes(token_tags, position_ids, grid, tile, heads, head_dim,

@@ -159,6 +159,7 @@ vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out) {
   out->scores_row_stride = lo.ns;
   out->chunk_offsets = lo.choff;
   out->state = lo.state;
+  out->qt = lo.qt;
   return VSA_OK;
 }
 
@@ -202,10 +203,15 @@ vsa_status vsa_h3_forward(const vsa_h3_plan* plan, const void* q, const void* k,
                               workspace_bytes, stream, nullptr);
 }
 
-vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const void* k,
-                                const void* v, const void* gate, vsa_dtype io_dtype, void* out,
-                                int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
-                                void* stream, void* const* events) {
+}  // extern "C"
+
+namespace {
+
+// The whole forward; `prep` is null, or the QK-norm + RoPE inputs.
+vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, const void* v,
+                       const void* gate, const vsa::QkPrepArgs* prep, vsa_dtype io_dtype,
+                       void* out, int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
+                       void* stream, void* const* events) {
   if (!plan) {
     set_error("plan is NULL");
     return VSA_E_ARG;
@@ -264,7 +270,12 @@ vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const vo
   };
   hipError_t err = mark(0);
   if (err != hipSuccess) return hip_fail("hipEventRecord", err);
-  vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, kt, vt, qp, kp, vp};
+  vsa::QkPrepArgs pp{};
+  if (prep) {
+    pp = *prep;
+    pp.qt = reinterpret_cast<uint16_t*>(ws + lo.qt);
+  }
+  vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, kt, vt, qp, kp, vp, pp};
   err = vsa::launch_permute_pool(pa, s);
   if (err != hipSuccess) return hip_fail("permute_pool launch", err);
   if ((err = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", err);
@@ -275,12 +286,68 @@ vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const vo
   if (err != hipSuccess) return hip_fail("coarse launch", err);
   if ((err = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
-  vsa::FineArgs fa{q, gate, out, f32, kt, vt, coarse, perm, valid, sel, choff, state,
+  vsa::FineArgs fa{q, pp.qt, gate, out, f32, kt, vt, coarse, perm, valid, sel, choff, state,
                    H, Nt, P, NV, topk, D, nchunks, chunk_tiles};
   err = vsa::launch_fine(fa, s);
   if (err != hipSuccess) return hip_fail("fine_attn launch", err);
   if ((err = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", err);
   return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const void* k,
+                                const void* v, const void* gate, vsa_dtype io_dtype, void* out,
+                                int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
+                                void* stream, void* const* events) {
+  return run_forward(plan, q, k, v, gate, nullptr, io_dtype, out, sel_idx, workspace,
+                     workspace_bytes, stream, events);
+}
+
+vsa_status vsa_h3_plan_set_qk_prep(vsa_h3_plan* plan, int32_t enable) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return VSA_E_ARG;
+  }
+  vsa::set_qk_prep(plan, enable != 0);
+  return VSA_OK;
+}
+
+vsa_status vsa_h3_forward_qk_prep(const vsa_h3_plan* plan, const void* q, const void* k,
+                                  const void* v, const void* gate, const float* q_norm_weight,
+                                  const float* k_norm_weight, float eps, const float* rope_cos,
+                                  const float* rope_sin, vsa_dtype io_dtype, void* out,
+                                  int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
+                                  void* stream, void* const* events) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return VSA_E_ARG;
+  }
+  if (!plan->qk_prep) {
+    set_error("the plan has no QK-norm + RoPE workspace: call vsa_h3_plan_set_qk_prep first");
+    return VSA_E_ARG;
+  }
+  if (plan->L > 0 && (!q_norm_weight || !k_norm_weight || !rope_cos || !rope_sin)) {
+    set_error("norm weights and RoPE tables must be non-NULL device pointers");
+    return VSA_E_ARG;
+  }
+  if (!(eps >= 0.0f) || eps > 3.0e38f) {
+    set_error("eps must be finite and >= 0");
+    return VSA_E_ARG;
+  }
+  for (const void* p : {static_cast<const void*>(q_norm_weight),
+                        static_cast<const void*>(k_norm_weight),
+                        static_cast<const void*>(rope_cos), static_cast<const void*>(rope_sin)}) {
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0) {
+      set_error("norm weights and RoPE tables must be 4-byte aligned");
+      return VSA_E_ARG;
+    }
+  }
+  vsa::QkPrepArgs prep{q_norm_weight, k_norm_weight, rope_cos, rope_sin, eps, nullptr};
+  return run_forward(plan, q, k, v, gate, &prep, io_dtype, out, sel_idx, workspace,
+                     workspace_bytes, stream, events);
 }
 
 vsa_status vsa_h3_oneshot_workspace_bytes(const int64_t* token_tags, const int64_t* position_ids,

@@ -211,13 +211,21 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   // A wave whose 32 query rows are all pad slots (the second half of a tile
   // with at most 32 valid tokens) only takes part in the loads and barriers.
   const bool active = 32 * w < valid[i];
+  // Rows come from the packed input, or from the tile-ordered copy that the
+  // gather wrote after QK-norm and RoPE (pad rows are zero there).
   bf16x8 qf[NCK];
+  if (a.qt) {
+    const uint16_t* qrow = a.qt + ((static_cast<size_t>(hd) * Nt + i) * 64 + 32 * w + l32) * D;
 #pragma unroll
-  for (int c = 0; c < NCK; ++c) {
-    if (pr >= 0)
-      qf[c] = IoOps<TIO>::load8(q + (static_cast<size_t>(pr) * H + hd) * D + 16 * c + 8 * hl);
-    else
-      qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int c = 0; c < NCK; ++c) qf[c] = IoOps<uint16_t>::load8(qrow + 16 * c + 8 * hl);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+      if (pr >= 0)
+        qf[c] = IoOps<TIO>::load8(q + (static_cast<size_t>(pr) * H + hd) * D + 16 * c + 8 * hl);
+      else
+        qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
   }
 
   const int32_t* sl = sel + (dense ? 0 : (static_cast<size_t>(hd) * NV + (i - P)) * topk);

@@ -6,6 +6,14 @@
 
 namespace vsa {
 
+// Optional QK-norm + RoPE applied while gathering (all null: not applied).
+struct QkPrepArgs {
+  const float *q_weight, *k_weight;  // [D]
+  const float *cos, *sin;            // [L][D/2], packed token order
+  float eps;
+  uint16_t* qt;                      // [H][Nt][64][D] bf16: normalised, rotated q
+};
+
 struct PermutePoolArgs {
   const void *q, *k, *v;        // [L][H][D], bf16 or fp32
   bool io_f32;
@@ -14,6 +22,7 @@ struct PermutePoolArgs {
   int H, Nt, D;
   uint16_t *kt, *vt;            // [H][Nt][64][D], [H][Nt][D][64] bf16
   float *qp, *kp, *vp;          // [H][Nt][D]
+  QkPrepArgs prep;
 };
 hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t stream);
 
@@ -29,7 +38,8 @@ struct CoarseArgs {
 hipError_t launch_coarse(const CoarseArgs& a, hipStream_t stream);
 
 struct FineArgs {
-  const void* q;                // [L][H][D] io dtype
+  const void* q;                // [L][H][D] io dtype (unused if qt is set)
+  const uint16_t* qt;           // [H][Nt][64][D] bf16 tile-ordered q, or null
   const void* gate;             // [L][H][D] io dtype
   void* out;                    // [L][H][D] io dtype
   bool io_f32;

@@ -17,6 +17,17 @@
 //     count.  That fixed order makes the pooled values, and therefore the
 //     top-k selection, reproducible bit for bit.
 // q itself is not permuted: the fine kernel gathers query rows directly.
+//
+// Optionally (PREP) q and k are first put through QK-norm and RoPE on the
+// staged rows (FastH3 NVFP4 on RTX PRO 6000, "Model integration": both are
+// applied to tile-ordered q and k with per-step cos/sin tables; pad rows stay
+// zero), in a fixed fp32 order so that the pooled values stay reproducible:
+//   ss = sum_d x_d * x_d (sequential, separately rounded), inv = 1 /
+//   sqrt(ss / D + eps) (each step correctly rounded), y_d = (x_d * inv) * w_d,
+//   then each interleaved pair (a, b) = (y_2i, y_2i+1) becomes
+//   (a*c - b*s, a*s + b*c) with the token's cos/sin;
+// the results replace the staged rows (rounded to the I/O type), so pooling,
+// Kt and the tile-ordered copy of q (Qt, for the fine kernel) all use them.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -24,16 +35,27 @@ namespace vsa {
 
 namespace {
 
-template <typename T, int D>
+__device__ __forceinline__ void store_pair(uint16_t* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+}
+__device__ __forceinline__ void store_pair(float* p, float a, float b) {
+  p[0] = a;
+  p[1] = b;
+}
+
+template <typename T, int D, bool PREP>
 __global__ __launch_bounds__(384) void permute_pool_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ valid, int H, int Nt,
     uint16_t* __restrict__ kt, uint16_t* __restrict__ vt, float* __restrict__ qp,
-    float* __restrict__ kp, float* __restrict__ vp) {
+    float* __restrict__ kp, float* __restrict__ vp, QkPrepArgs prep) {
   constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
   constexpr int kChunksPerRow = kRowBytes / 16;
   constexpr int kChunksPerTensor = 64 * kChunksPerRow;
-  __shared__ __attribute__((aligned(16))) T lds[3][64][D];
+  // Rows padded by 16 bytes: the per-row norm pass reads one column of 64
+  // rows at a time, which would otherwise fall into a single LDS bank.
+  constexpr int kPad = 16 / static_cast<int>(sizeof(T));
+  __shared__ __attribute__((aligned(16))) T lds[3][64][D + kPad];
 
   const int h = blockIdx.x;
   const int j = blockIdx.y;
@@ -41,23 +63,98 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
   const int n = valid[j];
   const int32_t* tperm = perm + static_cast<size_t>(j) * 64;
 
-  // Stage q, k, v rows of this tile (16-byte chunks, 256 B contiguous per row).
-  for (int c = tid; c < 3 * kChunksPerTensor; c += blockDim.x) {
+  // Stage q, k, v rows of this tile (16-byte chunks, a whole row contiguous
+  // in memory): the slot table first, then every load of this thread before
+  // any LDS store, so that the loads are in flight together.
+  __shared__ int sperm[64];
+  if (tid < 64) sperm[tid] = tid < n ? tperm[tid] : -1;
+  __syncthreads();
+  static_assert((3 * kChunksPerTensor) % 384 == 0, "staging split");
+  constexpr int PER = 3 * kChunksPerTensor / 384;
+  uint4 val[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int c = tid + 384 * r;
     const int x = c / kChunksPerTensor;
     const int rem = c - x * kChunksPerTensor;
     const int slot = rem / kChunksPerRow;
     const int part = rem - slot * kChunksPerRow;
     const T* src = x == 0 ? q : (x == 1 ? k : v);
-    uint4 val = make_uint4(0, 0, 0, 0);
-    const int r = slot < n ? tperm[slot] : -1;
-    if (r >= 0) {
-      const char* p = reinterpret_cast<const char*>(src) +
-                      (static_cast<size_t>(r) * H + h) * kRowBytes + part * 16;
-      val = *reinterpret_cast<const uint4*>(p);
-    }
-    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&lds[x][slot][0]) + part * 16) = val;
+    const int row = sperm[slot];
+    val[r] = make_uint4(0, 0, 0, 0);
+    if (row >= 0)
+      val[r] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) +
+                                               (static_cast<size_t>(row) * H + h) * kRowBytes +
+                                               part * 16);
+  }
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int c = tid + 384 * r;
+    const int x = c / kChunksPerTensor;
+    const int rem = c - x * kChunksPerTensor;
+    const int slot = rem / kChunksPerRow;
+    const int part = rem - slot * kChunksPerRow;
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&lds[x][slot][0]) + part * 16) = val[r];
   }
   __syncthreads();
+
+  if constexpr (PREP) {
+    __shared__ float rinv[2][64];
+    // Each thread's cos/sin entries for the rotation below, requested up
+    // front so that they arrive while the norms are computed (q and k of one
+    // (slot, pair) share them).
+    constexpr int PAIRS = D / 2;
+    constexpr int ITER = (64 * PAIRS + 383) / 384;
+    float cs[ITER], sn[ITER];
+#pragma unroll
+    for (int r = 0; r < ITER; ++r) {
+      const int c = tid + 384 * r;
+      const int s = c / PAIRS;
+      cs[r] = 1.0f;
+      sn[r] = 0.0f;
+      if (c < 64 * PAIRS && s < n) {
+        const size_t t = static_cast<size_t>(sperm[s]) * PAIRS + (c - s * PAIRS);
+        cs[r] = prep.cos[t];
+        sn[r] = prep.sin[t];
+      }
+    }
+    // Inverse RMS of every valid q and k row, one thread per row.
+    if (tid < 128) {
+      const int x = tid >> 6, s = tid & 63;
+      float inv = 0.0f;
+      if (s < n) {
+#pragma clang fp contract(off)
+        float ss = 0.0f;
+        for (int d = 0; d < D; ++d) {
+          const float e = to_f32(lds[x][s][d]);
+          ss = ss + e * e;
+        }
+        const float ms = __fdiv_rn(ss, static_cast<float>(D));
+        inv = __fdiv_rn(1.0f, __builtin_sqrtf(ms + prep.eps));   // IEEE (correctly rounded)
+      }
+      rinv[x][s] = inv;
+    }
+    __syncthreads();
+    // Scale, weight and rotate every interleaved pair of the valid rows.
+#pragma unroll
+    for (int r = 0; r < ITER; ++r) {
+      const int c = tid + 384 * r;
+      const int s = c / PAIRS;
+      const int i = c - s * PAIRS;
+      if (c < 64 * PAIRS && s < n) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+#pragma clang fp contract(off)
+          const float inv = rinv[x][s];
+          const float* w = x == 0 ? prep.q_weight : prep.k_weight;
+          const float a = (to_f32(lds[x][s][2 * i]) * inv) * w[2 * i];
+          const float b = (to_f32(lds[x][s][2 * i + 1]) * inv) * w[2 * i + 1];
+          store_pair(&lds[x][s][2 * i], a * cs[r] - b * sn[r], a * sn[r] + b * cs[r]);
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   const size_t tile_base = static_cast<size_t>(h) * Nt + j;
 
@@ -75,17 +172,17 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
     dst[tile_base * D + d] = mean;
   }
 
-  // Kt: [slot][d] bf16, 16-byte chunks of 8 channels.
-  {
-    uint16_t* dst = kt + tile_base * 64 * D;
+  // Kt (and Qt with PREP): [slot][d] bf16, 16-byte chunks of 8 channels.
+  for (int x = PREP ? 0 : 1; x < 2; ++x) {
+    uint16_t* dst = (x == 0 ? prep.qt : kt) + tile_base * 64 * D;
     for (int c = tid; c < 64 * (D / 8); c += blockDim.x) {
       const int slot = c / (D / 8);
       const int d0 = (c - slot * (D / 8)) * 8;
       uint4 o;
-      o.x = pack_bf16x2(to_f32(lds[1][slot][d0 + 0]), to_f32(lds[1][slot][d0 + 1]));
-      o.y = pack_bf16x2(to_f32(lds[1][slot][d0 + 2]), to_f32(lds[1][slot][d0 + 3]));
-      o.z = pack_bf16x2(to_f32(lds[1][slot][d0 + 4]), to_f32(lds[1][slot][d0 + 5]));
-      o.w = pack_bf16x2(to_f32(lds[1][slot][d0 + 6]), to_f32(lds[1][slot][d0 + 7]));
+      o.x = pack_bf16x2(to_f32(lds[x][slot][d0 + 0]), to_f32(lds[x][slot][d0 + 1]));
+      o.y = pack_bf16x2(to_f32(lds[x][slot][d0 + 2]), to_f32(lds[x][slot][d0 + 3]));
+      o.z = pack_bf16x2(to_f32(lds[x][slot][d0 + 4]), to_f32(lds[x][slot][d0 + 5]));
+      o.w = pack_bf16x2(to_f32(lds[x][slot][d0 + 6]), to_f32(lds[x][slot][d0 + 7]));
       *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
     }
   }
@@ -111,10 +208,16 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
 template <typename T, int D>
 hipError_t launch(const PermutePoolArgs& a, hipStream_t stream) {
   dim3 grid(a.H, a.Nt);
-  hipLaunchKernelGGL((permute_pool_kernel<T, D>), grid, dim3(384), 0, stream,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.kt, a.vt, a.qp,
-                     a.kp, a.vp);
+  if (a.prep.qt)
+    hipLaunchKernelGGL((permute_pool_kernel<T, D, true>), grid, dim3(384), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.kt, a.vt,
+                       a.qp, a.kp, a.vp, a.prep);
+  else
+    hipLaunchKernelGGL((permute_pool_kernel<T, D, false>), grid, dim3(384), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.kt, a.vt,
+                       a.qp, a.kp, a.vp, a.prep);
   return hipGetLastError();
 }
 

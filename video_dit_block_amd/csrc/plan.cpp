@@ -61,6 +61,7 @@ void lay_out(vsa_h3_plan* plan) {
   lo.state = take(chunked ? h64 * nt64 * 2 * 64 *
                                 static_cast<uint64_t>(state_words_per_lane(plan->head_dim)) * 4
                           : 0);
+  lo.qt = take(plan->qk_prep ? h64 * nt64 * kTile * d64 * 2 : 0);
   lo.total = off < 256 ? 256 : off;
   lo.ns = ns;
 }
@@ -92,6 +93,11 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
   plan->num_chunks = static_cast<int32_t>(nc);
   lay_out(plan);
   return VSA_OK;
+}
+
+void set_qk_prep(vsa_h3_plan* plan, bool enable) {
+  plan->qk_prep = enable;
+  lay_out(plan);
 }
 
 vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_dims3 grid,

@@ -24,7 +24,7 @@ constexpr int kMaxKeyChunks = 63;      // chunk boundaries one wave writes per q
 constexpr uint64_t kChunkBytes = uint64_t(10) << 20;
 
 struct Layout {
-  uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, total;
+  uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, qt, total;
   int64_t ns;  // scores row stride
 };
 
@@ -44,6 +44,7 @@ struct vsa_h3_plan {
   std::vector<int32_t> tile_slot;  // [L]
   int32_t chunk_tiles = 0;         // key tiles per fine-branch chunk
   int32_t num_chunks = 0;          // ceil(Nt / chunk_tiles); 0 when Nt == 0
+  bool qk_prep = false;            // workspace holds Qt for the QK-norm + RoPE forward
   vsa::Layout layout{};
 };
 
@@ -59,6 +60,10 @@ int64_t topk_rule(int64_t num_video_tiles, double sparsity);
 // Sets the key-chunk size of the fine branch (0 = automatic) and lays out
 // the workspace again.
 vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles);
+
+// Adds (or drops) the workspace region of the tile-ordered, normalised and
+// rotated q used by the QK-norm + RoPE forward.
+void set_qk_prep(vsa_h3_plan* plan, bool enable);
 
 vsa_status build_plan(const int64_t* token_tags, const int64_t* position_ids, int64_t L,
                       vsa_dims3 grid, vsa_dims3 tile, int32_t heads, int32_t head_dim,
