@@ -375,11 +375,14 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     // Lane holds keys 32b + 8(r/4) + 4hl + r%4 of query column l32; 16-key
     // chunk e is registers 8(e%2)..8(e%2)+7 of block e/2.
     if (active && (nj & 15)) {
+      // Key 32b + 8(r/4) + 4hl + r%4 is a pad key iff its constant part
+      // reaches nj - 4hl (one per-lane limit, not one index per register).
+      const int lim = nj - 4 * hl;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * b + 8 * (r >> 2) + 4 * hl + (r & 3) >= nj) sacc[b][r] = -INFINITY;
+          if (32 * b + 8 * (r >> 2) + (r & 3) >= lim) sacc[b][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
