@@ -12,5 +12,6 @@ from .vsa_h3 import (  # noqa: F401
     TEXT, COND, AUDIO, VIDEO,
     Geometry, GeometryError, geometry, topk_count, to_f32, pool_canonical,
     scores_canonical, select_topk, key_tiles, fine_item, fine, coarse, combine,
-    round_bf16_from_f64, forward, forward_head, qk_norm_rope, prep_qk,
+    round_bf16_from_f64, forward, forward_head, qk_norm_rope, prep_qk, e4m3_encode,
+    e4m3_decode, quantize_rows, dequantize_rows, E4M3_MAX,
 )

@@ -73,6 +73,20 @@ RoPE frequencies, so both arrive as inputs:
      nearest-even, or kept fp32) and are then the attention inputs: the
      pooling, scores, selection and fine branch all use them; v is unchanged.
 
+Optional 8-bit Q/K for the fine branch (the OmniRef page, section
+"Fallbacks": per-token FP8 Q/K with bf16 P.V, which its Blackwell profiles
+use for prefix rows):
+  R19 the format is OCP FP8 E4M3 (bias 7, 3 mantissa bits, subnormals, max
+     448, no infinities); encoding rounds to nearest with ties to the even
+     code and saturates at +-448;
+  R20 per-token scales: for every (token, head) row x of q and of k,
+     amax = max_d |x_d| (fp32); inv = fl32(448 / amax); code_d =
+     E4M3(fl32(x_d * inv)); the dequantisation scale is s = fl32(amax / 448);
+     a zero row has s = 0 and zero codes;
+  R21 only the fine branch uses the quantised values s * decode(code) for
+     its logits; pooling, scores, selection, the coarse branch and P.V
+     (bf16 V) are unchanged, and so is the 1/sqrt(D) scale.
+
 Pins (tests/test_oracle_pins.py) -- each function is checked against
 something other than itself:
   topk_count         closed-form values and the double-evaluation case
@@ -89,6 +103,13 @@ something other than itself:
                      all-equal pooled keys -> mean of pooled values
   combine            gate 0 -> out == o; tile-constant inputs, gate 1 ->
                      out == 2 * dense; per-channel gates
+  e4m3_encode/decode codes printed in the OCP definition (0, smallest
+                     subnormal, 1, 448, NaN...); every finite code round
+                     trips; every midpoint rounds to the even code (exact
+                     rationals); torch's float8_e4m3fn cast in range;
+                     saturation
+  quantize_rows      the largest element maps to +-448 exactly; relative
+                     error at most 2^-4 for normal codes; zero rows
   qk_norm_rope       a hand-computed 2-channel row; exact invariance under
                      power-of-two scaling (eps 0); unit RMS with unit
                      weights; identity and quarter-turn tables; one pair
@@ -347,6 +368,58 @@ def qk_norm_rope(x32: np.ndarray, weight: np.ndarray, eps: float, cos: np.ndarra
     return out
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """OCP FP8 E4M3 code (uint8) -> float64 (R19): sign, 4-bit exponent with
+    bias 7, 3-bit mantissa; exponent 0 is subnormal; S.1111.111 is NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = e4m3_decode(np.arange(127))        # the 127 finite non-negative values, ascending
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float64 -> OCP FP8 E4M3 code, nearest with ties to the even code,
+    saturating at +-448 (R19).  NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a == _E4M3_POS[hi], hi, np.where(pick_hi, hi, lo)).astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return np.where(np.isnan(x), 0x7F, code).astype(np.uint8)
+
+
+def quantize_rows(x32: np.ndarray):
+    """Per-row FP8 quantisation of R20.  x32 [N, D] fp32 -> (codes uint8
+    [N, D], scale fp32 [N])."""
+    x = np.asarray(x32, dtype=np.float32)
+    f32 = np.float32
+    amax = np.abs(x).max(axis=1)
+    nz = amax > 0
+    inv = np.where(nz, np.divide(f32(E4M3_MAX), np.where(nz, amax, f32(1)), dtype=f32), f32(0))
+    y = np.multiply(x, inv[:, None], dtype=f32)
+    codes = e4m3_encode(y.astype(np.float64))
+    scale = np.where(nz, np.divide(amax, f32(E4M3_MAX), dtype=f32), f32(0)).astype(np.float32)
+    return codes, scale
+
+
+def dequantize_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """s * decode(code), float64 [N, D] (R20, R21)."""
+    return scale.astype(np.float64)[:, None] * e4m3_decode(codes)
+
+
 def round_bf16_from_f64(x: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bfloat16 (ties to even), returned as
     float64.  One rounding step, straight from float64."""
@@ -373,8 +446,9 @@ class HeadResult:
 
 
 def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
-                 with_fine: bool = True) -> HeadResult:
-    """The whole forward for head h.  q, k, v, gate: [L, H, D] (torch or numpy)."""
+                 with_fine: bool = True, qk_fp8: bool = False) -> HeadResult:
+    """The whole forward for head h.  q, k, v, gate: [L, H, D] (torch or numpy).
+    qk_fp8: the fine branch uses per-token FP8 q and k (R19-R21)."""
     qh = to_f32(q[:, h, :])
     kh = to_f32(k[:, h, :])
     vh = to_f32(v[:, h, :])
@@ -388,8 +462,12 @@ def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
     c = coarse(S, vp, scale)
     o = out = None
     if with_fine:
-        o = fine(qh.astype(np.float64), kh.astype(np.float64), vh.astype(np.float64),
-                 geom, sel, scale, items)
+        if qk_fp8:
+            q64 = dequantize_rows(*quantize_rows(qh))
+            k64 = dequantize_rows(*quantize_rows(kh))
+        else:
+            q64, k64 = qh.astype(np.float64), kh.astype(np.float64)
+        o = fine(q64, k64, vh.astype(np.float64), geom, sel, scale, items)
         out = combine(o, to_f32(gate[:, h, :]), c, geom)
     return HeadResult(qp, kp, vp, S, sel, c, o, out)
 

@@ -556,3 +556,90 @@ def test_rope_rotates_adjacent_channel_pairs_of_the_input():
         assert np.array_equal(z[:, other], y[:, other])
         assert np.array_equal(z[:, 2 * i], -y[:, 2 * i + 1])
         assert np.array_equal(z[:, 2 * i + 1], y[:, 2 * i])
+
+
+# ----------------------------------------------------------------- FP8 (OCP E4M3) Q/K for the fine branch
+def test_e4m3_decode_printed_codes():
+    # values fixed by the OCP FP8 definition: bias 7, 3 mantissa bits, subnormals, max 448
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0x77: 240.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in table.items():
+        assert oracle.e4m3_decode(np.array([c]))[0] == v, hex(c)
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+    assert np.signbit(oracle.e4m3_decode(np.array([0x80]))[0])
+
+
+def test_e4m3_round_trip_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    assert np.array_equal(oracle.e4m3_encode(vals), codes)
+    assert np.all(np.diff(vals[:127]) > 0)            # monotone magnitudes 0..448
+
+
+def test_e4m3_midpoints_round_to_even_code_exactly():
+    from fractions import Fraction
+    vals = oracle.e4m3_decode(np.arange(127))
+    for c in range(126):
+        mid = (Fraction(vals[c]) + Fraction(vals[c + 1])) / 2
+        got = int(oracle.e4m3_encode(np.array([float(mid)]))[0])
+        assert float(mid) == mid                        # exactly representable in float64
+        assert got == (c if c % 2 == 0 else c + 1), (c, float(mid), got)
+        # just off the midpoint: the nearer value wins
+        assert oracle.e4m3_encode(np.array([float(mid) * (1 - 2 ** -40)]))[0] == c
+        assert oracle.e4m3_encode(np.array([float(mid) * (1 + 2 ** -40)]))[0] == c + 1
+
+
+def test_e4m3_matches_torch_cast_in_range_and_saturates():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.standard_normal(20000) * 30, rng.standard_normal(2000) * 1e-2,
+                        rng.uniform(-463.9, 463.9, 2000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(x.astype(np.float64)), ref)
+    assert list(oracle.e4m3_encode(np.array([464.0, 1e4, -1e9]))) == [0x7E, 0x7E, 0xFE]
+
+
+def test_quantize_rows_scale_max_and_error_bound():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((64, 128)) * rng.uniform(0.01, 50, (64, 1))).astype(np.float32)
+    x[3] = 0.0
+    codes, s = oracle.quantize_rows(x)
+    assert s[3] == 0 and not codes[3].any()
+    deq = oracle.dequantize_rows(codes, s)
+    rows = [r for r in range(64) if r != 3]
+    for r in rows:
+        j = int(np.argmax(np.abs(x[r])))
+        assert codes[r, j] & 0x7F == 0x7E                # the largest element becomes +-448
+        assert s[r] == np.float32(np.abs(x[r]).max() / np.float32(448.0))
+    # relative error of a normal code is at most 2^-4 (half of the 2^-3 mantissa step),
+    # plus the fp32 roundings of the scaling
+    normal = np.abs(oracle.e4m3_decode(codes)) >= 2.0 ** -6
+    err = np.abs(deq - x.astype(np.float64))
+    assert np.all(err[normal] <= (2.0 ** -4 + 1e-6) * np.abs(x.astype(np.float64))[normal])
+
+
+def test_fp8_fine_branch_close_to_full_precision_and_exact_on_representable_inputs():
+    # inputs whose rows already are exact FP8 multiples of a power-of-two scale
+    # (every |x| <= 448 * 2^-k on the E4M3 grid with the row max at 448 * 2^-k)
+    # quantise without error, so the FP8 fine branch equals the bf16 one
+    w = small_workload(D=32)
+    x = make_inputs(w, seed=2)
+    rng = np.random.default_rng(8)
+    L, H, D = w.L, w.heads, w.head_dim
+    codes = rng.integers(0, 126, (L, H, D)).astype(np.uint8) | rng.choice([0, 0x80], (L, H, D)).astype(np.uint8)
+    codes[:, :, 0] = 0x7E
+    qe = (oracle.e4m3_decode(codes) * 2.0 ** -6).astype(np.float32)
+    codes2 = rng.integers(0, 126, (L, H, D)).astype(np.uint8)
+    codes2[:, :, 5] = 0x7E
+    ke = (oracle.e4m3_decode(codes2) * 2.0 ** -5).astype(np.float32)
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
+    topk = oracle.topk_count(g.NV, w.sparsity)
+    for h in range(H):
+        a = oracle.forward_head(qe, ke, x["v"], x["gate"], g, topk, h)
+        b = oracle.forward_head(qe, ke, x["v"], x["gate"], g, topk, h, qk_fp8=True)
+        assert np.array_equal(a.sel, b.sel)
+        assert np.allclose(a.out, b.out, rtol=0, atol=1e-12)
+    # and on N(0,1) inputs the FP8 branch stays within a few per cent of full precision
+    r0 = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, 0)
+    r1 = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, 0, qk_fp8=True)
+    rel = np.linalg.norm(r1.out - r0.out) / np.linalg.norm(r0.out)
+    assert 1e-4 < rel < 5e-2
