@@ -94,6 +94,10 @@ typedef struct {
                        internal layout */
   uint64_t qt;      /* bf16 [H][Nt][64][D]: q after QK-norm + RoPE, tile order, pad rows zero
                        (only with vsa_h3_plan_set_qk_prep) */
+  uint64_t kt8;     /* uint8 [H][Nt][64][D]: keys as OCP E4M3 codes, tile order, pad rows zero
+                       (only with vsa_h3_plan_set_qk_fp8) */
+  uint64_t kscale;  /* fp32 [H][Nt][64]: per-key dequantisation scale amax/448, pad slots zero
+                       (only with vsa_h3_plan_set_qk_fp8) */
 } vsa_h3_ws_layout;
 
 /* Top-k rule of VSA-H3 evaluated in IEEE double as written; 0 when
@@ -228,6 +232,19 @@ vsa_status vsa_h3_forward_qk_prep(const vsa_h3_plan* plan, const void* q, const 
                                   const float* rope_sin, vsa_dtype io_dtype, void* out,
                                   int32_t* sel_idx, void* workspace, uint64_t workspace_bytes,
                                   void* stream, void* const* events);
+
+/* Optional 8-bit Q/K in the fine branch (the OmniRef page, "Fallbacks":
+ * per-token FP8 Q/K with bf16 P.V).  With vsa_h3_plan_set_qk_fp8(plan, 1)
+ * every forward of this plan (vsa_h3_forward, _timed, _qk_prep) computes the
+ * fine-branch logits from per-token OCP FP8 E4M3 q and k:
+ *   for each (token, head) row x of q and of k: amax = max_d |x_d|;
+ *   code_d = E4M3(x_d * (448 / amax)) (division correctly rounded, product
+ *   rounded to fp32, E4M3 rounding to nearest even); scale = amax / 448;
+ *   logit = scale_q * scale_k * sum_d decode(q_code_d) * decode(k_code_d) / sqrt(D).
+ * Pooling, scores, selection, the coarse branch and P.V (bf16) are unchanged.
+ * The workspace size changes (regions kt8 and kscale): call before sizing and
+ * uploading a workspace; 0 switches back to bf16 q and k. */
+vsa_status vsa_h3_plan_set_qk_fp8(vsa_h3_plan* plan, int32_t enable);
 
 void vsa_h3_plan_destroy(vsa_h3_plan* plan);
 const char* vsa_h3_last_error(void);

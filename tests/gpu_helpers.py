@@ -32,12 +32,13 @@ def to_dev(x, dev="cuda"):
     return {k: (v.to(dev) if k in ("q", "k", "v", "gate") else v) for k, v in x.items()}
 
 
-def run(x, grid, sparsity, dev="cuda", plan=None):
+def run(x, grid, sparsity, dev="cuda", plan=None, qk_fp8=False, chunk_tiles=0):
     """GPU forward through the C ABI.  Returns (out, sel, plan, workspace)."""
     xd = {k: x[k].to(dev) for k in ("q", "k", "v", "gate")}
     L, H, D = xd["q"].shape
     if plan is None:
-        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity)
+        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity,
+                        chunk_tiles=chunk_tiles, qk_fp8=qk_fp8)
     out, sel = vsa.forward(xd["q"], xd["k"], xd["v"], xd["gate"], plan=plan, return_sel=True)
     torch.cuda.synchronize()
     ws = plan.workspace(xd["q"].device)

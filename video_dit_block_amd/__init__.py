@@ -27,6 +27,7 @@ from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
     vsa_h3_oneshot_workspace_bytes, vsa_h3_plan_create, vsa_h3_plan_destroy, vsa_h3_plan_info,
     vsa_h3_plan_layout, vsa_h3_plan_set_chunk_tiles, vsa_h3_plan_tables, vsa_h3_plan_upload,
     vsa_h3_topk, vsa_h3_version, vsa_h3_plan_set_qk_prep, vsa_h3_forward_qk_prep,
+    vsa_h3_plan_set_qk_fp8,
 )
 
 __all__ = ["Plan", "forward", "forward_qk_prep", "VsaError", "vsa_h3_topk",
@@ -47,7 +48,8 @@ class Plan:
     """Tile geometry for one packed layout (host), plus per-device workspaces."""
 
     def __init__(self, token_tags, position_ids, grid, heads, head_dim, sparsity,
-                 tile=(4, 4, 4), chunk_tiles: int = 0, qk_prep: bool = False):
+                 tile=(4, 4, 4), chunk_tiles: int = 0, qk_prep: bool = False,
+                 qk_fp8: bool = False):
         self.token_tags = _host_i64(token_tags).reshape(-1)
         self.position_ids = _host_i64(position_ids).reshape(-1, 3)
         self.grid = tuple(int(g) for g in grid)
@@ -60,6 +62,9 @@ class Plan:
         if qk_prep:
             vsa_h3_plan_set_qk_prep(self.handle, True)
         self.qk_prep = bool(qk_prep)
+        if qk_fp8:
+            vsa_h3_plan_set_qk_fp8(self.handle, True)
+        self.qk_fp8 = bool(qk_fp8)
         self.info = vsa_h3_plan_info(self.handle)
         self.layout = vsa_h3_plan_layout(self.handle)
         self._ws = {}

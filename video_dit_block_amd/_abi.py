@@ -26,6 +26,7 @@ EXPORTED = (
     "vsa_h3_plan_tables", "vsa_h3_plan_upload", "vsa_h3_forward", "vsa_h3_forward_timed",
     "vsa_h3_oneshot_workspace_bytes", "vsa_h3_forward_oneshot", "vsa_h3_plan_destroy",
     "vsa_h3_last_error", "vsa_h3_version", "vsa_h3_plan_set_qk_prep", "vsa_h3_forward_qk_prep",
+    "vsa_h3_plan_set_qk_fp8",
 )
 
 
@@ -51,7 +52,8 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("perm", "valid", "kt", "vt", "qp", "kp", "vp",
                                                "scores", "coarse", "sel", "total")] + \
                [("scores_row_stride", ctypes.c_int64), ("chunk_offsets", ctypes.c_uint64),
-                ("state", ctypes.c_uint64), ("qt", ctypes.c_uint64)]
+                ("state", ctypes.c_uint64), ("qt", ctypes.c_uint64), ("kt8", ctypes.c_uint64),
+                ("kscale", ctypes.c_uint64)]
 
 
 _lib = None
@@ -96,6 +98,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_double, Dims3, ctypes.c_int, _P, _P, _P,
                                              ctypes.c_uint64, _P]
         L.vsa_h3_plan_set_qk_prep.argtypes = [_P, ctypes.c_int32]
+        L.vsa_h3_plan_set_qk_fp8.argtypes = [_P, ctypes.c_int32]
         L.vsa_h3_forward_qk_prep.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                              ctypes.c_int, _P, _P, _P, ctypes.c_uint64, _P,
                                              ctypes.POINTER(_P)]
@@ -191,6 +194,10 @@ def vsa_h3_forward_timed(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr
 
 def vsa_h3_plan_set_qk_prep(plan: int, enable: bool) -> None:
     check(lib().vsa_h3_plan_set_qk_prep(plan, 1 if enable else 0))
+
+
+def vsa_h3_plan_set_qk_fp8(plan: int, enable: bool) -> None:
+    check(lib().vsa_h3_plan_set_qk_fp8(plan, 1 if enable else 0))
 
 
 def vsa_h3_forward_qk_prep(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr: int,

@@ -160,6 +160,8 @@ vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out) {
   out->chunk_offsets = lo.choff;
   out->state = lo.state;
   out->qt = lo.qt;
+  out->kt8 = lo.kt8;
+  out->kscale = lo.kscale;
   return VSA_OK;
 }
 
@@ -275,7 +277,10 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
     pp = *prep;
     pp.qt = reinterpret_cast<uint16_t*>(ws + lo.qt);
   }
-  vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, kt, vt, qp, kp, vp, pp};
+  uint8_t* kt8 = plan->qk_fp8 ? reinterpret_cast<uint8_t*>(ws + lo.kt8) : nullptr;
+  float* kscale = plan->qk_fp8 ? reinterpret_cast<float*>(ws + lo.kscale) : nullptr;
+  vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, kt, vt, qp, kp, vp, pp, kt8,
+                          kscale};
   err = vsa::launch_permute_pool(pa, s);
   if (err != hipSuccess) return hip_fail("permute_pool launch", err);
   if ((err = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", err);
@@ -287,7 +292,7 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
   if ((err = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
   vsa::FineArgs fa{q, pp.qt, gate, out, f32, kt, vt, coarse, perm, valid, sel, choff, state,
-                   H, Nt, P, NV, topk, D, nchunks, chunk_tiles};
+                   H, Nt, P, NV, topk, D, nchunks, chunk_tiles, kt8, kscale};
   err = vsa::launch_fine(fa, s);
   if (err != hipSuccess) return hip_fail("fine_attn launch", err);
   if ((err = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", err);
@@ -312,6 +317,15 @@ vsa_status vsa_h3_plan_set_qk_prep(vsa_h3_plan* plan, int32_t enable) {
     return VSA_E_ARG;
   }
   vsa::set_qk_prep(plan, enable != 0);
+  return VSA_OK;
+}
+
+vsa_status vsa_h3_plan_set_qk_fp8(vsa_h3_plan* plan, int32_t enable) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return VSA_E_ARG;
+  }
+  vsa::set_qk_fp8(plan, enable != 0);
   return VSA_OK;
 }
 

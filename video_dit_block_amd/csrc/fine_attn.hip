@@ -156,18 +156,41 @@ constexpr int kWaitVm = 0x0F70;
 __device__ __forceinline__ int swz128(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz256(int row) { return row & 15; }
 
-template <typename TIO, int D>
+// Swizzle of the 16-byte chunks of one key row in LDS (physical chunk =
+// logical chunk ^ kswz(row)): conflict-free MFMA operand reads for 256-byte
+// (bf16, D 128), 128-byte (bf16 D 64, or FP8 D 128) and 64-byte rows.
+template <int ROW_BYTES, bool FP8ROWS>
+__device__ __forceinline__ int kswz(int row) {
+  if (FP8ROWS) return ROW_BYTES == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+  return ROW_BYTES == 256 ? swz256(row) : swz128(row);
+}
+
+// Eight input values as fp32.
+template <typename TIO>
+__device__ __forceinline__ void load_f32x8(const TIO* p, float v[8]) {
+  IoOps<TIO>::load4(p, v);
+  IoOps<TIO>::load4(p + 4, v + 4);
+}
+
+template <typename TIO, int D, bool QK8>
 __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
                                                           const int32_t* __restrict__ valid,
                                                           const int32_t* __restrict__ sel,
                                                           const int32_t* __restrict__ choff,
                                                           float* __restrict__ state, int chunk) {
-  constexpr int KROW = D / 8;                  // 16-byte chunks per K row
-  constexpr int TILE_BYTES = 64 * D * 2;       // one K (or V^T) tile
-  constexpr int LOADS = TILE_BYTES / 1024 / 2; // 1 KB DMA loads per wave per tile
+  constexpr int TILE_BYTES = 64 * D * 2;       // one bf16 K (or V^T) tile
+  constexpr int LOADS = TILE_BYTES / 1024 / 2; // 1 KB DMA loads per wave per V^T tile
+  // K rows: bf16 (2D bytes), or OCP FP8 E4M3 codes (D bytes) with QK8.
+  constexpr int KROWB = QK8 ? D : 2 * D;
+  constexpr int KROW = KROWB / 16;             // 16-byte chunks per K row
+  constexpr int K_TILE = 64 * KROWB;
+  constexpr int KLOADS = K_TILE / 1024 / 2;    // 1 KB DMA loads per wave per K tile
+  constexpr int NK64 = D / 64;                 // FP8 MFMA steps of 64 channels
   constexpr int NCK = D / 16;                  // QK contraction steps
   constexpr int NB = D / 32;                   // O^T blocks of 32 channels
-  __shared__ __attribute__((aligned(1024))) char lds_k[TILE_BYTES];
+  // With QK8 the K tile is followed by 1 KB per wave for the per-key scales
+  // (the first 128 bytes of each hold the wave's 32 scales).
+  __shared__ __attribute__((aligned(1024))) char lds_k[QK8 ? K_TILE + 2048 : K_TILE];
   __shared__ __attribute__((aligned(1024))) char lds_v[TILE_BYTES];
 
   const int tid = threadIdx.x;
@@ -213,8 +236,48 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   const bool active = 32 * w < valid[i];
   // Rows come from the packed input, or from the tile-ordered copy that the
   // gather wrote after QK-norm and RoPE (pad rows are zero there).
-  bf16x8 qf[NCK];
-  if (a.qt) {
+  bf16x8 qf[QK8 ? 1 : NCK];
+  // QK8: this lane's 64 channels 64m + 32hl + 0..31 (m < NK64) of its query
+  // row as E4M3 codes of x * (448 / amax) (amax over the whole row), and the
+  // row's dequantisation scale amax / 448 (zero rows: zero codes and scale).
+  i32x8 qf8[QK8 ? NK64 : 1];
+  float qsc = 1.0f;
+  if constexpr (QK8) {
+    float x[NK64][32];
+#pragma unroll
+    for (int m = 0; m < NK64; ++m)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 64 * m + 32 * hl + 8 * g;
+        if (a.qt) {
+          load_f32x8(a.qt + ((static_cast<size_t>(hd) * Nt + i) * 64 + 32 * w + l32) * D + d0,
+                     &x[m][8 * g]);
+        } else if (pr >= 0) {
+          load_f32x8(q + (static_cast<size_t>(pr) * H + hd) * D + d0, &x[m][8 * g]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[m][8 * g + e] = 0.0f;
+        }
+      }
+    float amax = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NK64; ++m)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[m][e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float inv = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
+    qsc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 0.0f;
+#pragma unroll
+    for (int m = 0; m < NK64; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(x[m][4 * j] * inv, x[m][4 * j + 1] * inv, 0,
+                                                     false);
+        u = __builtin_amdgcn_cvt_pk_fp8_f32(x[m][4 * j + 2] * inv, x[m][4 * j + 3] * inv, u,
+                                            true);
+        qf8[m][j] = static_cast<int>(u);
+      }
+  } else if (a.qt) {
     const uint16_t* qrow = a.qt + ((static_cast<size_t>(hd) * Nt + i) * 64 + 32 * w + l32) * D;
 #pragma unroll
     for (int c = 0; c < NCK; ++c) qf[c] = IoOps<uint16_t>::load8(qrow + 16 * c + 8 * hl);
@@ -229,7 +292,10 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   }
 
   const int32_t* sl = sel + (dense ? 0 : (static_cast<size_t>(hd) * NV + (i - P)) * topk);
-  const char* kth = reinterpret_cast<const char*>(a.kt) + static_cast<size_t>(hd) * Nt * TILE_BYTES;
+  const char* kth = (QK8 ? reinterpret_cast<const char*>(a.kt8) : reinterpret_cast<const char*>(a.kt)) +
+                    static_cast<size_t>(hd) * Nt * K_TILE;
+  const char* ksh =
+      QK8 ? reinterpret_cast<const char*>(a.kscale) + static_cast<size_t>(hd) * Nt * 256 : nullptr;
   const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nt * TILE_BYTES;
   // Listed ids are clamped into [0, Nt): a corrupt list can give a wrong
   // result but never an out-of-bounds read.
@@ -242,18 +308,17 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   // fetches the global chunk that the swizzle places there.  The swizzle term
   // repeats every KREP (VREP) loads, so a few base offsets plus a constant
   // stride cover all of them.  Wave w fills K rows 32w..32w+31.
-  constexpr int KREP = D == 128 ? 4 : 2;
-  constexpr int KSTEP = D == 128 ? 16 * 256 : 16 * 128;   // rows per KREP loads x row bytes
-  constexpr int KROWS_PER_LOAD = 1024 / (D * 2);
+  constexpr int KROWS_PER_LOAD = 1024 / KROWB;
+  constexpr int KREP = 16 / KROWS_PER_LOAD;                // the K swizzle repeats every 16 rows
+  constexpr int KSTEP = 16 * KROWB;
   constexpr int VREP = 2;
   constexpr int VSTEP = 16 * 128;
   int kbase[KREP], vbase[VREP], vmin[VREP];
 #pragma unroll
   for (int e = 0; e < KREP; ++e) {
-    const int p = (w * LOADS + e) * 64 + lane;
+    const int p = (w * KLOADS + e) * 64 + lane;
     const int key = p / KROW, pc = p % KROW;
-    const int kswz = D == 128 ? swz256(key) : swz128(key);
-    kbase[e] = key * (D * 2) + ((pc ^ kswz) << 4);
+    kbase[e] = key * KROWB + ((pc ^ kswz<KROWB, QK8>(key)) << 4);
   }
 #pragma unroll
   for (int e = 0; e < VREP; ++e) {
@@ -278,12 +343,21 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 // V^T: every load is issued, so that its count stays fixed, but lanes whose
 // chunk lies in a 16-key group without valid keys stay idle; P.V never reads
 // those groups, so their stale contents (possibly non-finite) cannot leak.
-#define VSA_LOAD_K(SRC, NKL)                                                                  \
-  _Pragma("unroll") for (int e = 0; e < LOADS; ++e) {                                          \
-    if (e < (NKL))                                                                             \
+// With QK8 every wave also requests its 32 per-key scales (one load, lanes
+// 8..63 repeating lanes 0..7), so a K group is NKL + 1 loads.
+#define VSA_LOAD_K(J, NKL)                                                                    \
+  {                                                                                            \
+    const char* src_ = kth + static_cast<size_t>(J) * K_TILE;                                  \
+    _Pragma("unroll") for (int e = 0; e < KLOADS; ++e) {                                       \
+      if (e < (NKL))                                                                           \
+        __builtin_amdgcn_global_load_lds(                                                      \
+            (gbl_void*)(src_ + (e / KREP) * KSTEP + kbase[e % KREP]),                          \
+            (lds_void*)(lds_k + (w * KLOADS + e) * 1024), 16, 0, 0);                           \
+    }                                                                                          \
+    if (QK8)                                                                                   \
       __builtin_amdgcn_global_load_lds(                                                        \
-          (gbl_void*)((SRC) + (e / KREP) * KSTEP + kbase[e % KREP]),                           \
-          (lds_void*)(lds_k + (w * LOADS + e) * 1024), 16, 0, 0);                              \
+          (gbl_void*)(ksh + static_cast<size_t>(J) * 256 + 128 * w + 16 * (lane & 7)),         \
+          (lds_void*)(lds_k + K_TILE + 1024 * w), 16, 0, 0);                                   \
   }
 #define VSA_LOAD_V(SRC, NJ)                                                                   \
   _Pragma("unroll") for (int e = 0; e < LOADS; ++e) {                                          \
@@ -292,17 +366,19 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
           (gbl_void*)((SRC) + (e / VREP) * VSTEP + vbase[e % VREP]),                           \
           (lds_void*)(lds_v + (w * LOADS + e) * 1024), 16, 0, 0);                              \
   }
-  // K loads this wave issues for a tile with n valid keys.
+  // K tile loads this wave issues for a tile with n valid keys.
   auto k_loads = [&](int n) -> int {
     const int rows = n - 32 * w;
-    return rows <= 0 ? 0 : min(LOADS, (rows + KROWS_PER_LOAD - 1) / KROWS_PER_LOAD);
+    return rows <= 0 ? 0 : min(KLOADS, (rows + KROWS_PER_LOAD - 1) / KROWS_PER_LOAD);
   };
 
   // Per-lane LDS read offsets of the MFMA operands.
-  const int kswz_r = D == 128 ? swz256(l32) : swz128(l32);
+  const int kswz_r = kswz<KROWB, QK8>(l32);
   const int vswz_r = swz128(l32);
 
-  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  // Logit scale in log2 units; with QK8 it also carries the query row's
+  // dequantisation scale (the key scales are applied to S below).
+  const float scale_log2 = (1.4426950408889634f / sqrtf(static_cast<float>(D))) * qsc;
   // Running state of this wave's 32 rows: O^T accumulators, running max (in
   // log2 units) and this lane's partial row sum.  Between key-chunk launches
   // it lives in `state`, one 16-byte quad per lane per 4 words, coalesced:
@@ -337,7 +413,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   if (beg < end) {
     j = tile_at(beg);
     nj = valid[j];
-    VSA_LOAD_K(kth + static_cast<size_t>(j) * TILE_BYTES, k_loads(nj));
+    VSA_LOAD_K(j, k_loads(nj));
     VSA_LOAD_V(vth + static_cast<size_t>(j) * TILE_BYTES, nj);
   }
   // Query and state registers (and the first tile) have landed.
@@ -355,12 +431,37 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       if (active && (b == 0 || nj > 32)) {
-        const char* krow = lds_k + (32 * b + l32) * (D * 2);
+        const char* krow = lds_k + (32 * b + l32) * KROWB;
+        if constexpr (QK8) {
+          // Scale bytes 127 (2^0): plain E4M3 x E4M3 products, fp32 sums.
 #pragma unroll
-        for (int c = 0; c < NCK; ++c) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (((2 * c + hl) ^ kswz_r) << 4));
-          sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? f32x16{} : sacc[b],
-                                                            0, 0, 0);
+          for (int m = 0; m < NK64; ++m) {
+            const int lc = 4 * m + 2 * hl;
+            const u32x4 k0 = *reinterpret_cast<const u32x4*>(krow + ((lc ^ kswz_r) << 4));
+            const u32x4 k1 = *reinterpret_cast<const u32x4*>(krow + (((lc + 1) ^ kswz_r) << 4));
+            const i32x8 kf = __builtin_bit_cast(
+                i32x8, u32x8{k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w});
+            sacc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                kf, qf8[m], m == 0 ? f32x16{} : sacc[b], 0, 0, 0, 127, 0, 127);
+          }
+          // Key dequantisation scales (before the pad mask: pad scales are 0).
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 ks = *reinterpret_cast<const f32x4*>(lds_k + K_TILE + 1024 * b +
+                                                             4 * (8 * r4 + 4 * hl));
+            sacc[b][4 * r4 + 0] *= ks.x;
+            sacc[b][4 * r4 + 1] *= ks.y;
+            sacc[b][4 * r4 + 2] *= ks.z;
+            sacc[b][4 * r4 + 3] *= ks.w;
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NCK; ++c) {
+            const bf16x8 kf =
+                *reinterpret_cast<const bf16x8*>(krow + (((2 * c + hl) ^ kswz_r) << 4));
+            sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c],
+                                                              c == 0 ? f32x16{} : sacc[b], 0, 0, 0);
+          }
         }
       }
     }
@@ -370,7 +471,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     const int jn = it + 1 < end ? tile_at(it + 1) : j;
     const int njn = valid[jn];
     const int kl_next = k_loads(njn);
-    VSA_LOAD_K(kth + static_cast<size_t>(jn) * TILE_BYTES, kl_next);
+    VSA_LOAD_K(jn, kl_next);
 
     // Lane holds keys 32b + 8(r/4) + 4hl + r%4 of query column l32; 16-key
     // chunk e is registers 8(e%2)..8(e%2)+7 of block e/2.
@@ -424,8 +525,8 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     }
     l_run += psum;
 
-    // V(t) landed (the kl_next loads of K(t+1) may still be in flight).
-    switch (kl_next) {
+    // V(t) landed (the K(t+1) group may still be in flight).
+    switch (kl_next + (QK8 ? 1 : 0)) {
       case 0: __builtin_amdgcn_s_waitcnt(kWaitVm | 0); break;
       case 1: __builtin_amdgcn_s_waitcnt(kWaitVm | 1); break;
       case 2: __builtin_amdgcn_s_waitcnt(kWaitVm | 2); break;
@@ -502,17 +603,22 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   }
 }
 
-template <typename TIO, int D>
-hipError_t launch(const FineArgs& a, hipStream_t stream) {
+template <typename TIO, int D, bool QK8>
+hipError_t launch_q(const FineArgs& a, hipStream_t stream) {
   const int blocks = a.H * a.Nt;
   const int nchunks = a.nchunks > 1 ? a.nchunks : 1;
   for (int c = 0; c < nchunks; ++c) {
-    hipLaunchKernelGGL((fine_attn_kernel<TIO, D>), dim3(blocks), dim3(128), 0, stream, a,
+    hipLaunchKernelGGL((fine_attn_kernel<TIO, D, QK8>), dim3(blocks), dim3(128), 0, stream, a,
                        a.valid, a.sel, a.choff, a.state, c);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+template <typename TIO, int D>
+hipError_t launch(const FineArgs& a, hipStream_t stream) {
+  return a.kt8 ? launch_q<TIO, D, true>(a, stream) : launch_q<TIO, D, false>(a, stream);
 }
 
 }  // namespace

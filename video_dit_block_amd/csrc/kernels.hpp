@@ -23,6 +23,8 @@ struct PermutePoolArgs {
   uint16_t *kt, *vt;            // [H][Nt][64][D], [H][Nt][D][64] bf16
   float *qp, *kp, *vp;          // [H][Nt][D]
   QkPrepArgs prep;
+  uint8_t* kt8;                 // [H][Nt][64][D] E4M3 keys instead of kt, or null
+  float* kscale;                // [H][Nt][64] per-key scale (with kt8)
 };
 hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t stream);
 
@@ -53,6 +55,8 @@ struct FineArgs {
   float* state;                 // running softmax state between chunks (nchunks > 1)
   int H, Nt, P, NV, topk, D;
   int nchunks, chunk_tiles;
+  const uint8_t* kt8;           // [H][Nt][64][D] E4M3 keys: FP8 Q/K logits, or null
+  const float* kscale;          // [H][Nt][64]
 };
 hipError_t launch_fine(const FineArgs& a, hipStream_t stream);
 

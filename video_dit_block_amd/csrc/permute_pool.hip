@@ -48,7 +48,8 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ valid, int H, int Nt,
     uint16_t* __restrict__ kt, uint16_t* __restrict__ vt, float* __restrict__ qp,
-    float* __restrict__ kp, float* __restrict__ vp, QkPrepArgs prep) {
+    float* __restrict__ kp, float* __restrict__ vp, QkPrepArgs prep, uint8_t* __restrict__ kt8,
+    float* __restrict__ kscale) {
   constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
   constexpr int kChunksPerRow = kRowBytes / 16;
   constexpr int kChunksPerTensor = 64 * kChunksPerRow;
@@ -172,8 +173,40 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
     dst[tile_base * D + d] = mean;
   }
 
+  // Keys as per-token FP8 (OCP E4M3) codes instead of bf16: amax of each
+  // valid row, codes of x * (448 / amax) (the division correctly rounded, the
+  // product rounded to fp32, the conversion to nearest even), and the
+  // dequantisation scale amax / 448; pad rows get zero codes and scale.
+  if (kt8) {
+    __shared__ float kinv[64];
+    if (tid < 64) {
+      float amax = 0.0f;
+      if (tid < n)
+        for (int d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(to_f32(lds[1][tid][d])));
+      kinv[tid] = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
+      kscale[tile_base * 64 + tid] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 0.0f;
+    }
+    __syncthreads();
+    uint8_t* dst = kt8 + tile_base * 64 * D;
+    for (int c = tid; c < 64 * (D / 16); c += blockDim.x) {
+      const int slot = c / (D / 16);
+      const int d0 = (c - slot * (D / 16)) * 16;
+      const float inv = kinv[slot];
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const T* e = &lds[1][slot][d0 + 4 * j];
+        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(to_f32(e[0]) * inv, to_f32(e[1]) * inv, 0,
+                                                     false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(to_f32(e[2]) * inv, to_f32(e[3]) * inv, w, true);
+        o[j] = w;
+      }
+      *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
+    }
+  }
+
   // Kt (and Qt with PREP): [slot][d] bf16, 16-byte chunks of 8 channels.
-  for (int x = PREP ? 0 : 1; x < 2; ++x) {
+  for (int x = PREP ? 0 : 1; x < (kt8 ? 1 : 2); ++x) {
     uint16_t* dst = (x == 0 ? prep.qt : kt) + tile_base * 64 * D;
     for (int c = tid; c < 64 * (D / 8); c += blockDim.x) {
       const int slot = c / (D / 8);
@@ -212,12 +245,12 @@ hipError_t launch(const PermutePoolArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((permute_pool_kernel<T, D, true>), grid, dim3(384), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.kt, a.vt,
-                       a.qp, a.kp, a.vp, a.prep);
+                       a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale);
   else
     hipLaunchKernelGGL((permute_pool_kernel<T, D, false>), grid, dim3(384), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.kt, a.vt,
-                       a.qp, a.kp, a.vp, a.prep);
+                       a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale);
   return hipGetLastError();
 }
 

@@ -62,6 +62,8 @@ void lay_out(vsa_h3_plan* plan) {
                                 static_cast<uint64_t>(state_words_per_lane(plan->head_dim)) * 4
                           : 0);
   lo.qt = take(plan->qk_prep ? h64 * nt64 * kTile * d64 * 2 : 0);
+  lo.kt8 = take(plan->qk_fp8 ? h64 * nt64 * kTile * d64 : 0);
+  lo.kscale = take(plan->qk_fp8 ? h64 * nt64 * kTile * 4 : 0);
   lo.total = off < 256 ? 256 : off;
   lo.ns = ns;
 }
@@ -97,6 +99,11 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
 
 void set_qk_prep(vsa_h3_plan* plan, bool enable) {
   plan->qk_prep = enable;
+  lay_out(plan);
+}
+
+void set_qk_fp8(vsa_h3_plan* plan, bool enable) {
+  plan->qk_fp8 = enable;
   lay_out(plan);
 }
 

@@ -24,7 +24,8 @@ constexpr int kMaxKeyChunks = 63;      // chunk boundaries one wave writes per q
 constexpr uint64_t kChunkBytes = uint64_t(10) << 20;
 
 struct Layout {
-  uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, qt, total;
+  uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, qt, kt8, kscale,
+      total;
   int64_t ns;  // scores row stride
 };
 
@@ -45,6 +46,7 @@ struct vsa_h3_plan {
   int32_t chunk_tiles = 0;         // key tiles per fine-branch chunk
   int32_t num_chunks = 0;          // ceil(Nt / chunk_tiles); 0 when Nt == 0
   bool qk_prep = false;            // workspace holds Qt for the QK-norm + RoPE forward
+  bool qk_fp8 = false;             // fine branch uses per-token FP8 q and k
   vsa::Layout layout{};
 };
 
@@ -64,6 +66,10 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles);
 // Adds (or drops) the workspace region of the tile-ordered, normalised and
 // rotated q used by the QK-norm + RoPE forward.
 void set_qk_prep(vsa_h3_plan* plan, bool enable);
+
+// Switches the fine branch to per-token FP8 (E4M3) q and k and adds the
+// regions of the quantised key tiles and their scales (or drops them).
+void set_qk_fp8(vsa_h3_plan* plan, bool enable);
 
 vsa_status build_plan(const int64_t* token_tags, const int64_t* position_ids, int64_t L,
                       vsa_dims3 grid, vsa_dims3 tile, int32_t heads, int32_t head_dim,
