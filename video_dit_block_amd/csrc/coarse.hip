@@ -133,18 +133,21 @@ __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(float* __restr
       key[m] = ok[m] ? order_key(s[m]) : 0u;
     }
     // Largest T with #{key >= T} >= topk, i.e. the topk-th largest key.
+    // Counts are ballots and popcounts (scalar unit), not lane sums.  Slots
+    // that are not video key tiles hold key 0, which no candidate (>= 1)
+    // reaches; every real key is nonzero (finite scores map above 2^23).
     uint32_t thr = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
       int c = 0;
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) c += (ok[m] && key[m] >= cand) ? 1 : 0;
-      if (wave_sum_i(c) >= topk) thr = cand;
+      for (int m = 0; m < MAXM; ++m) c += __popcll(__builtin_amdgcn_ballot_w64(key[m] >= cand));
+      if (c >= topk) thr = cand;
     }
     int gt = 0;
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m) gt += (ok[m] && key[m] > thr) ? 1 : 0;
-    const int need = topk - wave_sum_i(gt);  // ties to admit, lowest index first
+    for (int m = 0; m < MAXM; ++m) gt += __popcll(__builtin_amdgcn_ballot_w64(key[m] > thr));
+    const int need = topk - gt;  // ties to admit, lowest index first
     const uint64_t below = (uint64_t(1) << lane) - 1;
     // Lane c <= nchunks also counts the kept ids below c * chunk_tiles (the
     // key-chunk boundaries of the fine branch): the count before block xm
@@ -281,17 +284,26 @@ hipError_t launch_d(const CoarseArgs& a, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   const int rows = a.H * a.Nt;
   dim3 g2((rows + 3) / 4);
+  // Row registers per lane: the smallest instantiated multiple of 4 (up to
+  // 32, then of 8) covering ceil(Nt / 64).
   const int maxm = (a.Nt + 63) / 64;
-  if (maxm <= 4)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<4>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
-  else if (maxm <= 8)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<8>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
-  else if (maxm <= 16)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<16>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
-  else if (maxm <= 32)
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<32>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
-  else
-    hipLaunchKernelGGL((coarse_softmax_topk_kernel<64>), g2, dim3(256), 0, stream, a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks, a.chunk_tiles, a.choff);
+#define VSA_TOPK(M)                                                                           \
+  hipLaunchKernelGGL((coarse_softmax_topk_kernel<M>), g2, dim3(256), 0, stream, a.scores, a.H, \
+                     a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks,              \
+                     a.chunk_tiles, a.choff)
+  if (maxm <= 4) VSA_TOPK(4);
+  else if (maxm <= 8) VSA_TOPK(8);
+  else if (maxm <= 12) VSA_TOPK(12);
+  else if (maxm <= 16) VSA_TOPK(16);
+  else if (maxm <= 20) VSA_TOPK(20);
+  else if (maxm <= 24) VSA_TOPK(24);
+  else if (maxm <= 28) VSA_TOPK(28);
+  else if (maxm <= 32) VSA_TOPK(32);
+  else if (maxm <= 40) VSA_TOPK(40);
+  else if (maxm <= 48) VSA_TOPK(48);
+  else if (maxm <= 56) VSA_TOPK(56);
+  else VSA_TOPK(64);
+#undef VSA_TOPK
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
