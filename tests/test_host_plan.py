@@ -285,3 +285,21 @@ def test_qk_prep_plan_region_and_argument_errors():
                                     None) == _abi.VSA_E_WORKSPACE
     vsa.vsa_h3_plan_set_qk_prep(p2.handle, False)
     assert vsa.vsa_h3_plan_info(p2.handle).workspace_bytes == base
+
+
+def test_default_key_chunks_follow_the_key_format():
+    # FP8 keys are one byte per element: a 10 MiB chunk holds 64*128*(1+2) = 24 KB tiles
+    w = WORKLOADS["768p10s"]
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity, qk_fp8=True)
+    assert (p.chunk_tiles, p.num_chunks) == (426, 3)
+    assert p.chunk_tiles * 64 * w.head_dim * 3 <= 10 << 20
+    lo = p.layout
+    assert lo.kt8 % 256 == 0 and lo.kscale % 256 == 0
+    assert lo.kscale + w.heads * p.num_tiles * 64 * 4 <= lo.total
+    # an explicit chunk length is kept when the key format changes
+    p2 = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity, chunk_tiles=200, qk_fp8=True)
+    assert (p2.chunk_tiles, p2.num_chunks) == (200, 7)
+    vsa.vsa_h3_plan_set_qk_fp8(p.handle, False)
+    info = vsa.vsa_h3_plan_info(p.handle)
+    assert (info.chunk_tiles, info.num_chunks) == (319, 4)

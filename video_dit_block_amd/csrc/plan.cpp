@@ -78,8 +78,10 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
   const int64_t Nt = plan->Nt;
   int64_t ch;
   if (chunk_tiles == 0) {
-    // Largest chunk within kChunkBytes, then balanced over the chunks.
-    const int64_t cap = static_cast<int64_t>(kChunkBytes / (uint64_t(256) * plan->head_dim));
+    // Largest chunk within kChunkBytes of K and V (64 keys x D: K in bf16,
+    // or FP8 codes, plus bf16 V^T), then balanced over the chunks.
+    const uint64_t tile_bytes = uint64_t(64) * plan->head_dim * (plan->qk_fp8 ? 3 : 4);
+    const int64_t cap = static_cast<int64_t>(kChunkBytes / tile_bytes);
     const int64_t nc = std::max<int64_t>(1, ceil_div(Nt, cap));
     ch = std::max<int64_t>(1, ceil_div(Nt, nc));
   } else {
@@ -91,6 +93,7 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
               " key chunks; at most " + std::to_string(kMaxKeyChunks) + " are supported");
     return VSA_E_ARG;
   }
+  plan->chunk_request = chunk_tiles;
   plan->chunk_tiles = static_cast<int32_t>(std::min<int64_t>(ch, std::max<int64_t>(Nt, 1)));
   plan->num_chunks = static_cast<int32_t>(nc);
   lay_out(plan);
@@ -104,7 +107,8 @@ void set_qk_prep(vsa_h3_plan* plan, bool enable) {
 
 void set_qk_fp8(vsa_h3_plan* plan, bool enable) {
   plan->qk_fp8 = enable;
-  lay_out(plan);
+  // An automatic chunk length depends on the key bytes per tile.
+  if (plan->chunk_request != 0 || set_chunk_tiles(plan, 0) != VSA_OK) lay_out(plan);
 }
 
 vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_dims3 grid,

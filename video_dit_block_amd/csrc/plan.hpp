@@ -44,6 +44,7 @@ struct vsa_h3_plan {
   std::vector<int32_t> valid;      // [Nt]
   std::vector<int32_t> tile_slot;  // [L]
   int32_t chunk_tiles = 0;         // key tiles per fine-branch chunk
+  int32_t chunk_request = 0;       // as last requested (0 = automatic)
   int32_t num_chunks = 0;          // ceil(Nt / chunk_tiles); 0 when Nt == 0
   bool qk_prep = false;            // workspace holds Qt for the QK-norm + RoPE forward
   bool qk_fp8 = false;             // fine branch uses per-token FP8 q and k
