@@ -250,6 +250,15 @@ def test_python_forward_refuses_cpu_tensors():
         vsa.forward(x, x, x, x, tags, pos, w.grid, w.sparsity)
 
 
+def test_more_than_4096_tiles_per_head_is_rejected():
+    ok = Workload("ok", 1, 64, "f32", (), (64, 64, 64), 0.5)          # 4,096 tiles
+    tags, pos = make_layout(ok)
+    assert vsa.Plan(tags, pos, ok.grid, 1, 64, 0.5).num_tiles == 4096
+    big = Workload("big", 1, 64, "f32", ((TEXT, 1),), (64, 64, 64), 0.5)   # 4,097 tiles
+    tags, pos = make_layout(big)
+    assert _raw_create(tags.numpy(), pos.numpy(), big.grid, heads=1, D=64) == _abi.VSA_E_UNSUPPORTED
+
+
 def test_qk_prep_plan_region_and_argument_errors():
     w = WORKLOADS["tiny"]
     tags, pos = make_layout(w)
