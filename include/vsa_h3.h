@@ -77,8 +77,9 @@ typedef struct {
   uint64_t perm;    /* int32 [Nt][64]: packed row of each tile slot, -1 for pad slots */
   uint64_t valid;   /* int32 [Nt]: valid tokens per tile */
   uint64_t kt;      /* bf16 [H][Nt][64][D]: keys in tile order, pad rows zero */
-  uint64_t vt;      /* bf16 [H][Nt][D][64]: values in tile order, transposed, pad columns zero;
-                       inside each 16-slot group the columns hold slots 0-3, 8-11, 4-7, 12-15 */
+  uint64_t vt;      /* bf16 [H][Nt][2][D][32]: values in tile order, transposed, in two halves
+                       of 32 slots (0-31, 32-63), pad columns zero; inside each 16-slot
+                       group the columns hold slots 0-3, 8-11, 4-7, 12-15 */
   uint64_t qp;      /* fp32 [H][Nt][D]: pooled (mean) q per tile */
   uint64_t kp;      /* fp32 [H][Nt][D]: pooled k */
   uint64_t vp;      /* fp32 [H][Nt][D]: pooled v */

@@ -76,7 +76,7 @@ def intermediates(plan, ws):
         "vp": plan.view(ws, "vp", torch.float32, (H, Nt, D)).cpu().numpy(),
         "coarse": plan.view(ws, "coarse", torch.float32, (H, Nt, D)).cpu().numpy(),
         "kt": plan.view(ws, "kt", torch.int16, (H, Nt, 64, D)).cpu(),
-        "vt": plan.view(ws, "vt", torch.int16, (H, Nt, D, 64)).cpu(),
+        "vt": plan.view(ws, "vt", torch.int16, (H, Nt, 2, D, 32)).cpu(),
         "probs": plan.view(ws, "scores", torch.float32, (H, Nt, ns)).cpu().numpy()[:, :, :Nt],
     }
 

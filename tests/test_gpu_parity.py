@@ -76,7 +76,10 @@ def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True, plan=None
             assert torch.equal(inter["kt"][h], kt_ref), f"K tiles head {h}"
             # V^T columns: inside each 16-slot group, slots 0-3, 8-11, 4-7, 12-15
             cols = [(p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1) for p in range(64)]
-            assert torch.equal(inter["vt"][h], vt_ref.transpose(1, 2)[:, :, cols]), f"V^T tiles head {h}"
+            # ... and two halves of 32 slots, each [D][32]
+            vt_cols = vt_ref.transpose(1, 2)[:, :, cols]
+            vt_halves = vt_cols.reshape(g.Nt, w.head_dim, 2, 32).permute(0, 2, 1, 3)
+            assert torch.equal(inter["vt"][h], vt_halves), f"V^T tiles head {h}"
     return out, sel, plan, ws
 
 

@@ -18,11 +18,12 @@
 //     registers;
 //   - the visit list is ascending (prefix tiles 0..P-1, then the selected
 //     video tiles), so every row starts from a finite running max;
-//   - K [64][D] and V^T [D][64] of the current key tile sit in two LDS
-//     regions filled by direct global->LDS loads (global_load_lds_dwordx4,
-//     no register staging).  K(t+1) is requested as soon as S(t) is computed
-//     and V(t+1) as soon as P(t).V(t) is done, so each load overlaps about
-//     half an iteration, and four blocks per CU cover the rest;
+//   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
+//     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
+//     global->LDS loads (global_load_lds_dwordx4, no register staging).  A
+//     slot is refilled with the next tile's half as soon as both waves have
+//     read it, so each load has about three quarters of an iteration to land
+//     (32 KB of LDS per block, four blocks per CU);
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so
 //     each lane holds one query column), online softmax in fp32 via exp2 with
 //     the 1/sqrt(D) scale folded into log2 units; the running max is raised
@@ -32,9 +33,15 @@
 //     accumulator layout; V^T is stored with the keys of each 16-key group
 //     permuted (0-3, 8-11, 4-7, 12-15) so that each lane's 8 keys are one
 //     16-byte LDS read;
-//   - LDS rows use XOR-swizzled 16-byte chunks, bank-conflict free for the
-//     MFMA operand reads;
-//   - partial key tiles skip their empty 16-key chunks entirely;
+//   - LDS slots are made of 64-byte rows with XOR-swizzled 16-byte chunks,
+//     bank-conflict free for the MFMA operand reads; one per-lane offset
+//     serves every DMA load of a slot;
+//   - each key tile is taken in two 32-key halves, and the exp of one half
+//     is issued between the MFMAs of the other (Q.K of the second half, then
+//     P.V of the first), so softmax arithmetic and matrix work can overlap
+//     inside each wave; a half without valid keys is skipped, and the
+//     running max is tested per lane, with the row's two lanes combined only
+//     when it has to rise;
 //   - blocks are mapped to the 8 XCDs so that each XCD works through its own
 //     heads, head by head: the 32 CUs of an XCD sweep the same head's K/V;
 //   - long key lists are cut into key chunks, one launch each: every query
@@ -44,6 +51,8 @@
 //     sums) is stored in fp32 at the end of a launch and loaded at the start
 //     of the next; visit order and arithmetic are those of a single launch,
 //     so the result is the same bit for bit.
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -151,18 +160,16 @@ __device__ __forceinline__ void decode_item_chunked(int b, int H, int Nt, int& h
 // conservative vmcnt(0) in front of the LDS reads.
 constexpr int kWaitVm = 0x0F70;
 
-// XOR swizzle of the 16-byte chunk index inside an LDS row, conflict free
-// for the operand reads of 8 (32 banks) or 16 (64 banks) consecutive rows.
-__device__ __forceinline__ int swz128(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int swz256(int row) { return row & 15; }
+// XOR swizzle of the 16-byte chunk index inside a 64-byte LDS row: rows
+// r, r + 4, r + 8, r + 12 differ, so the 16 lanes of one pass of a 16-byte
+// operand read (rows r0..r0+15, one chunk each) hit all 64 banks once.
+__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
 
-// Swizzle of the 16-byte chunks of one key row in LDS (physical chunk =
-// logical chunk ^ kswz(row)): conflict-free MFMA operand reads for 256-byte
-// (bf16, D 128), 128-byte (bf16 D 64, or FP8 D 128) and 64-byte rows.
-template <int ROW_BYTES, bool FP8ROWS>
-__device__ __forceinline__ int kswz(int row) {
-  if (FP8ROWS) return ROW_BYTES == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
-  return ROW_BYTES == 256 ? swz256(row) : swz128(row);
+// An opaque copy of x: no instruction is emitted, but code that uses the
+// result cannot be moved above this point (for instance out of a branch).
+__device__ __forceinline__ float pinned(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Eight input values as fp32.
@@ -178,20 +185,25 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
                                                           const int32_t* __restrict__ sel,
                                                           const int32_t* __restrict__ choff,
                                                           float* __restrict__ state, int chunk) {
-  constexpr int TILE_BYTES = 64 * D * 2;       // one bf16 K (or V^T) tile
-  constexpr int LOADS = TILE_BYTES / 1024 / 2; // 1 KB DMA loads per wave per V^T tile
   // K rows: bf16 (2D bytes), or OCP FP8 E4M3 codes (D bytes) with QK8.
   constexpr int KROWB = QK8 ? D : 2 * D;
-  constexpr int KROW = KROWB / 16;             // 16-byte chunks per K row
   constexpr int K_TILE = 64 * KROWB;
-  constexpr int KLOADS = K_TILE / 1024 / 2;    // 1 KB DMA loads per wave per K tile
-  constexpr int NK64 = D / 64;                 // FP8 MFMA steps of 64 channels
-  constexpr int NCK = D / 16;                  // QK contraction steps
-  constexpr int NB = D / 32;                   // O^T blocks of 32 channels
-  // With QK8 the K tile is followed by 1 KB per wave for the per-key scales
-  // (the first 128 bytes of each hold the wave's 32 scales).
-  __shared__ __attribute__((aligned(1024))) char lds_k[QK8 ? K_TILE + 2048 : K_TILE];
-  __shared__ __attribute__((aligned(1024))) char lds_v[TILE_BYTES];
+  constexpr int KH_BYTES = 32 * KROWB;           // one 32-key half of a K tile
+  constexpr int VH_BYTES = 64 * D;               // one 32-key half of a V^T tile: D rows of 64 B
+  constexpr int V_TILE = 2 * VH_BYTES;
+  constexpr int KH_LOADS = KH_BYTES / 1024 / 2;  // 1 KB DMA loads per wave per K half
+  constexpr int VH_LOADS = VH_BYTES / 1024 / 2;  // the same per V^T half
+  constexpr int NK64 = D / 64;                   // FP8 MFMA steps of 64 channels
+  constexpr int NCK = D / 16;                    // QK contraction steps
+  constexpr int NB = D / 32;                     // O^T blocks of 32 channels
+  // Four LDS slots, one per half tile: K keys 0-31, K keys 32-63, V^T keys
+  // 0-31 and V^T keys 32-63.  With QK8 a K slot is followed by 1 KB per wave
+  // for per-key scales (the first 64 bytes hold the wave's 16 scales).
+  constexpr int KSLOT = QK8 ? KH_BYTES + 2048 : KH_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds_ka[KSLOT];
+  __shared__ __attribute__((aligned(1024))) char lds_kb[KSLOT];
+  __shared__ __attribute__((aligned(1024))) char lds_va[VH_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_vb[VH_BYTES];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -296,7 +308,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
                     static_cast<size_t>(hd) * Nt * K_TILE;
   const char* ksh =
       QK8 ? reinterpret_cast<const char*>(a.kscale) + static_cast<size_t>(hd) * Nt * 256 : nullptr;
-  const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nt * TILE_BYTES;
+  const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nt * V_TILE;
   // Listed ids are clamped into [0, Nt): a corrupt list can give a wrong
   // result but never an out-of-bounds read.
   auto tile_at = [&](int it) -> int {
@@ -304,77 +316,77 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     return min(max(t, 0), Nt - 1);
   };
 
-  // Per-lane source offsets of the DMA loads: the lane that fills LDS chunk p
-  // fetches the global chunk that the swizzle places there.  The swizzle term
-  // repeats every KREP (VREP) loads, so a few base offsets plus a constant
-  // stride cover all of them.  Wave w fills K rows 32w..32w+31.
-  constexpr int KROWS_PER_LOAD = 1024 / KROWB;
-  constexpr int KREP = 16 / KROWS_PER_LOAD;                // the K swizzle repeats every 16 rows
-  constexpr int KSTEP = 16 * KROWB;
-  constexpr int VREP = 2;
-  constexpr int VSTEP = 16 * 128;
-  int kbase[KREP], vbase[VREP], vmin[VREP];
-#pragma unroll
-  for (int e = 0; e < KREP; ++e) {
-    const int p = (w * KLOADS + e) * 64 + lane;
-    const int key = p / KROW, pc = p % KROW;
-    kbase[e] = key * KROWB + ((pc ^ kswz<KROWB, QK8>(key)) << 4);
-  }
-#pragma unroll
-  for (int e = 0; e < VREP; ++e) {
-    const int p = (w * LOADS + e) * 64 + lane;
-    const int d = p >> 3, pv = p & 7;
-    const int lc = pv ^ swz128(d);               // logical chunk: positions 8lc..8lc+7
-    vbase[e] = d * 128 + (lc << 4);
-    // The P.V step reads whole 16-key groups (pad slots included, which are
-    // zero in memory): a chunk is needed iff its group holds a valid key.
-    vmin[e] = 16 * (lc >> 1);
-  }
+  // LDS slot layouts (16-byte chunks, XOR-swizzled inside 64-byte rows so
+  // that the MFMA operand reads are free of bank conflicts):
+  //   K half:   [KROWB/64 groups][32 keys][64 B]: chunks 4G..4G+3 of a key
+  //             row; logical chunk c sits at (c ^ swz64(key)) in its group;
+  //   V^T half: [D rows][64 B] (the 32 keys of the half), the same swizzle.
+  // DMA load number x (0..2*LOADS-1 over both waves, 64 lanes x 16 B each)
+  // fills LDS chunks 64x..64x+63: K rows 16(x % 2) + lane/4 of group x/2,
+  // V^T rows 16x + lane/4.  The lane part of the source offset is the same
+  // for every load, the rest is uniform.
+  const int lane_sw = ((lane & 3) ^ ((lane >> 4) & 3)) << 4;
+  const int kbase = (lane >> 2) * KROWB + lane_sw;
+  const int vbase = (lane >> 2) * 64 + lane_sw;
 // Block barrier without the workgroup fence of __syncthreads(): the fence
 // would also wait for every outstanding global->LDS load, which this loop
 // keeps in flight on purpose.  LDS reads are drained first (so no wave's
 // pending read can race the next DMA into that region) and DMA completion is
-// awaited explicitly (kWaitVm) before the barriers that publish a tile.  The
+// awaited explicitly (kWaitVm) before the barriers that publish a slot.  The
 // memory clobber keeps the compiler from moving memory accesses across it.
 #define VSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-// K: only the loads whose rows hold valid keys (a count uniform per wave).
-// Scores of rows not loaded are never used: empty 16-key chunks are skipped
-// and pad keys inside a chunk are overwritten with -inf.
-// V^T: every load is issued, so that its count stays fixed, but lanes whose
-// chunk lies in a 16-key group without valid keys stay idle; P.V never reads
-// those groups, so their stale contents (possibly non-finite) cannot leak.
-// With QK8 every wave also requests its 32 per-key scales (one load, lanes
-// 8..63 repeating lanes 0..7), so a K group is NKL + 1 loads.
-#define VSA_LOAD_K(J, NKL)                                                                    \
+// Half B of K tile J into slot SLOT: KH_LOADS loads per wave and, with QK8,
+// one load of the wave's 16 per-key scales (lanes 4..63 repeat lanes 0..3).
+// Pad rows are zero in memory, so a loaded half holds no stale data; a half
+// without valid keys is neither loaded nor read.
+#define VSA_LOAD_KH(SLOT, J, B)                                                               \
   {                                                                                            \
-    const char* src_ = kth + static_cast<size_t>(J) * K_TILE;                                  \
-    _Pragma("unroll") for (int e = 0; e < KLOADS; ++e) {                                       \
-      if (e < (NKL))                                                                           \
-        __builtin_amdgcn_global_load_lds(                                                      \
-            (gbl_void*)(src_ + (e / KREP) * KSTEP + kbase[e % KREP]),                          \
-            (lds_void*)(lds_k + (w * KLOADS + e) * 1024), 16, 0, 0);                           \
+    const char* src_ = kth + static_cast<size_t>(J) * K_TILE + (B) * KH_BYTES;                 \
+    _Pragma("unroll") for (int e = 0; e < KH_LOADS; ++e) {                                     \
+      const int x_ = w * KH_LOADS + e;                                                         \
+      __builtin_amdgcn_global_load_lds(                                                        \
+          (gbl_void*)(src_ + kbase + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64),                  \
+          (lds_void*)((SLOT) + x_ * 1024), 16, 0, 0);                                          \
     }                                                                                          \
     if (QK8)                                                                                   \
       __builtin_amdgcn_global_load_lds(                                                        \
-          (gbl_void*)(ksh + static_cast<size_t>(J) * 256 + 128 * w + 16 * (lane & 7)),         \
-          (lds_void*)(lds_k + K_TILE + 1024 * w), 16, 0, 0);                                   \
+          (gbl_void*)(ksh + static_cast<size_t>(J) * 256 + 128 * (B) + 64 * w + 16 * (lane & 3)), \
+          (lds_void*)((SLOT) + KH_BYTES + 1024 * w), 16, 0, 0);                                \
   }
-#define VSA_LOAD_V(SRC, NJ)                                                                   \
-  _Pragma("unroll") for (int e = 0; e < LOADS; ++e) {                                          \
-    if (vmin[e % VREP] < (NJ))                                                                 \
-      __builtin_amdgcn_global_load_lds(                                                        \
-          (gbl_void*)((SRC) + (e / VREP) * VSTEP + vbase[e % VREP]),                           \
-          (lds_void*)(lds_v + (w * LOADS + e) * 1024), 16, 0, 0);                              \
+// Half B of V^T tile J into slot SLOT: VH_LOADS loads per wave.
+#define VSA_LOAD_VH(SLOT, J, B)                                                               \
+  {                                                                                            \
+    const char* src_ = vth + static_cast<size_t>(J) * V_TILE + (B) * VH_BYTES;                 \
+    _Pragma("unroll") for (int e = 0; e < VH_LOADS; ++e) {                                     \
+      const int x_ = w * VH_LOADS + e;                                                         \
+      __builtin_amdgcn_global_load_lds((gbl_void*)(src_ + vbase + x_ * 1024),                  \
+                                       (lds_void*)((SLOT) + x_ * 1024), 16, 0, 0);             \
+    }                                                                                          \
   }
-  // K tile loads this wave issues for a tile with n valid keys.
-  auto k_loads = [&](int n) -> int {
-    const int rows = n - 32 * w;
-    return rows <= 0 ? 0 : min(KLOADS, (rows + KROWS_PER_LOAD - 1) / KROWS_PER_LOAD);
+  // Loads this wave issues for half b of a tile with n valid keys.
+  constexpr int CK = KH_LOADS + (QK8 ? 1 : 0);
+  constexpr int CV = VH_LOADS;
+  static_assert(2 * (CK > CV ? CK : CV) <= 8, "wait counts above 8");
+  auto ck = [](int n, int b) -> int { return n > 32 * b ? CK : 0; };
+  auto cv = [](int n, int b) -> int { return n > 32 * b ? CV : 0; };
+  // Wait until at most n of this wave's loads are in flight.
+  auto wait_vm = [](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(kWaitVm | 0); break;
+      case 1: __builtin_amdgcn_s_waitcnt(kWaitVm | 1); break;
+      case 2: __builtin_amdgcn_s_waitcnt(kWaitVm | 2); break;
+      case 3: __builtin_amdgcn_s_waitcnt(kWaitVm | 3); break;
+      case 4: __builtin_amdgcn_s_waitcnt(kWaitVm | 4); break;
+      case 5: __builtin_amdgcn_s_waitcnt(kWaitVm | 5); break;
+      case 6: __builtin_amdgcn_s_waitcnt(kWaitVm | 6); break;
+      case 7: __builtin_amdgcn_s_waitcnt(kWaitVm | 7); break;
+      default: __builtin_amdgcn_s_waitcnt(kWaitVm | 8); break;
+    }
   };
 
-  // Per-lane LDS read offsets of the MFMA operands.
-  const int kswz_r = kswz<KROWB, QK8>(l32);
-  const int vswz_r = swz128(l32);
+  // Swizzle of this lane's operand rows (key l32 of a K half, V^T row
+  // 32n + l32; the latter does not depend on n).
+  const int rswz = swz64(l32);
 
   // Logit scale in log2 units; with QK8 it also carries the query row's
   // dequantisation scale (the key scales are applied to S below).
@@ -409,155 +421,272 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
       for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
   }
 
+  // A key tile is taken in two halves of 32 keys; each half is 8 Q.K MFMA
+  // steps (bf16; 2 with FP8 q/k) and 8 P.V steps (D 128).  The work of one
+  // tile runs as four phases, each a fixed sequence of steps fenced with
+  // sched_barrier so that the compiler keeps the order:
+  //   1. Q.K of half 0;
+  //   2. Q.K of half 1, with the exp of half 0 spread over its steps;
+  //   3. P.V of half 0, with the exp of half 1 spread over its steps;
+  //   4. P.V of half 1.
+  // The MFMA operands are read from LDS kAhead steps ahead of their use.
+  constexpr int kQkSteps = QK8 ? NK64 : NCK;
+  constexpr int kPvSteps = 2 * NB;
+  constexpr int kAhead = 2;
+  typedef typename std::conditional<QK8, i32x8, bf16x8>::type QkOp;
+
+  // LDS operand of Q.K step k of half b (lane row l32 of the half's keys).
+  auto qk_read = [&](int b, int k) -> QkOp {
+    const char* krow = (b ? lds_kb : lds_ka) + l32 * 64;
+    if constexpr (QK8) {
+      // Chunks 4k + 2hl and 4k + 2hl + 1 (channels 64k + 32hl + 0..31).
+      const char* g = krow + k * 2048;
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(g + (((2 * hl) ^ rswz) << 4));
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(g + (((2 * hl + 1) ^ rswz) << 4));
+      return __builtin_bit_cast(i32x8, u32x8{k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w});
+    } else {
+      // Chunk 2k + hl (channels 16k + 8hl + 0..7).
+      return *reinterpret_cast<const bf16x8*>(krow + (k >> 1) * 2048 +
+                                              (((2 * (k & 1) + hl) ^ rswz) << 4));
+    }
+  };
+  // Q.K step k: S^T (keys x queries) of the half accumulates channels of step k.
+  auto qk_step = [&](int k, const QkOp& kf, f32x16& acc) {
+    if constexpr (QK8) {
+      // Scale bytes 127 (2^0): plain E4M3 x E4M3 products, fp32 sums.
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[k], k == 0 ? f32x16{} : acc,
+                                                            0, 0, 0, 127, 0, 127);
+    } else {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], k == 0 ? f32x16{} : acc, 0, 0, 0);
+    }
+  };
+  // FP8 keys: multiply S by the per-key dequantisation scales (pad keys have
+  // scale 0 and are masked afterwards).  Keys 16v..16v+15 of the half were
+  // staged by wave v.
+  auto key_scales = [&](int b, f32x16& acc) {
+    if constexpr (QK8) {
+      const char* sc = (b ? lds_kb : lds_ka) + KH_BYTES;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 ks = *reinterpret_cast<const f32x4*>(sc + 1024 * (r4 >> 1) +
+                                                         4 * (8 * (r4 & 1) + 4 * hl));
+        acc[4 * r4 + 0] *= ks.x;
+        acc[4 * r4 + 1] *= ks.y;
+        acc[4 * r4 + 2] *= ks.z;
+        acc[4 * r4 + 3] *= ks.w;
+      }
+    }
+  };
+  // LDS operand of P.V step k of half b: V^T rows 32n.., 16-key group g of the half.
+  auto pv_read = [&](int b, int k) -> bf16x8 {
+    const int g = k / NB, n = k % NB;
+    const char* vrow = (b ? lds_vb : lds_va) + (32 * n + l32) * 64;
+    return *reinterpret_cast<const bf16x8*>(vrow + (((2 * g + hl) ^ rswz) << 4));
+  };
+  auto pv_step = [&](int k, const bf16x8& vf, const bf16x8& pa, const bf16x8& pb) {
+    const int g = k / NB, n = k % NB;
+    oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, g == 0 ? pa : pb, oacc[n], 0, 0, 0);
+  };
+  // Softmax pairs [8k/NS, 8(k+1)/NS) of one half: p = exp2(s*scale - mref),
+  // packed to bf16 pair by pair (word r/2 of the two 16-key operands).
+  auto sm_part = [&](int k, int ns, const f32x16& sacc, float mref, uint32_t pw[8], float& ps) {
+#pragma unroll
+    for (int q = 8 * k / ns; q < 8 * (k + 1) / ns; ++q) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * q], scale_log2, -mref));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * q + 1], scale_log2, -mref));
+      ps += p0;
+      ps += p1;
+      pw[q] = pack_bf16x2(p0, p1);
+    }
+  };
+  // p <- bf16(p * f) for the 8 probabilities of one operand.
+  auto rescale_bf16 = [](bf16x8& p, float f) {
+    u32x4 u = __builtin_bit_cast(u32x4, p);
+    u.x = pack_bf16x2(__uint_as_float(u.x << 16) * f, __uint_as_float(u.x & 0xffff0000u) * f);
+    u.y = pack_bf16x2(__uint_as_float(u.y << 16) * f, __uint_as_float(u.y & 0xffff0000u) * f);
+    u.z = pack_bf16x2(__uint_as_float(u.z << 16) * f, __uint_as_float(u.z & 0xffff0000u) * f);
+    u.w = pack_bf16x2(__uint_as_float(u.w << 16) * f, __uint_as_float(u.w & 0xffff0000u) * f);
+    p = __builtin_bit_cast(bf16x8, u);
+  };
+  auto pack16 = [](const uint32_t pw[8], bf16x8& pa, bf16x8& pb) {
+    pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    pb = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+  };
+  // Q.K of half b; if SM, the softmax of the other half (s_other, reference
+  // mref) is spread over the steps.  Returns that softmax's lane sum.
+  auto qk_phase = [&](int b, f32x16& acc, bool sm, const f32x16& s_other, float mref,
+                      bf16x8& pa, bf16x8& pb) -> float {
+    QkOp kf[kQkSteps];
+    uint32_t pv[8];
+    float ps = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kAhead && k < kQkSteps; ++k) kf[k] = qk_read(b, k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kQkSteps; ++k) {
+      if (k + kAhead < kQkSteps) kf[k + kAhead] = qk_read(b, k + kAhead);
+      qk_step(k, kf[k], acc);
+      if (sm) sm_part(k, kQkSteps, s_other, mref, pv, ps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    key_scales(b, acc);
+    if (sm) pack16(pv, pa, pb);
+    return ps;
+  };
+  // P.V of half b (probabilities pa, pb); if SM, the softmax of s_other is
+  // spread over the steps.  Returns that softmax's lane sum.
+  auto pv_phase = [&](int b, const bf16x8& pa, const bf16x8& pb, bool sm, const f32x16& s_other,
+                      float mref, bf16x8& qa, bf16x8& qb) -> float {
+    bf16x8 vf[kPvSteps];
+    uint32_t pv[8];
+    float ps = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) vf[k] = pv_read(b, k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kPvSteps; ++k) {
+      if (k + kAhead < kPvSteps) vf[k + kAhead] = pv_read(b, k + kAhead);
+      pv_step(k, vf[k], pa, pb);
+      if (sm) sm_part(k, kPvSteps, s_other, mref, pv, ps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (sm) pack16(pv, qa, qb);
+    return ps;
+  };
+  // Pad keys (index >= nj) of half b to -inf: key 32b + 8(r/4) + 4hl + r%4
+  // is a pad key iff its constant part reaches nj - 32b - 4hl.
+  auto mask_half = [&](f32x16& acc, int b, int n) {
+    const int lim = n - 32 * b - 4 * hl;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) >= lim) acc[r] = -INFINITY;
+  };
+  auto max16 = [](const f32x16& acc) -> float {
+    float m = acc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[r]);
+    return m;
+  };
+  // New running max (log2 units) when some row of the wave has a score more
+  // than 2^8 above it, else m_run itself.  Each lane tests its own 16 keys
+  // of a row; only then are the two halves of each row (lanes l, l ^ 32)
+  // combined, so the common case needs no cross-lane exchange.
+  auto raised_max = [&](float mx_lane) -> float {
+    if (__builtin_amdgcn_ballot_w64(mx_lane * scale_log2 > m_run + 8.0f) == 0) return m_run;
+    const float mx = fmaxf(mx_lane, __shfl_xor(mx_lane, 32));
+    return fmaxf(m_run, mx * scale_log2);
+  };
+
   int j = 0, nj = 0;
   if (beg < end) {
     j = tile_at(beg);
     nj = valid[j];
-    VSA_LOAD_K(j, k_loads(nj));
-    VSA_LOAD_V(vth + static_cast<size_t>(j) * TILE_BYTES, nj);
+    VSA_LOAD_KH(lds_ka, j, 0);
+    if (nj > 32) VSA_LOAD_KH(lds_kb, j, 1);
+    VSA_LOAD_VH(lds_va, j, 0);
   }
-  // Query and state registers (and the first tile) have landed.
+  // Query and state registers (and the first tile's halves) have landed.
   __builtin_amdgcn_s_waitcnt(kWaitVm);
 
+  // Slot ring: each half tile is requested as soon as its slot has been read
+  // by both waves, about three quarters of an iteration before it is needed.
+  // Issue order, in iteration t: V^T half 1 of t, then K half 0, K half 1 and
+  // V^T half 0 of t + 1; each wait below counts the loads issued after the
+  // half it needs.
+  const f32x16 kNone = {};
   for (int it = beg; it < end; ++it) {
-    const int nchunk = active ? (nj + 15) >> 4 : 0;   // 16-key chunks to process
-    // K(t) landed (V(t) may still be in flight).
-    __builtin_amdgcn_s_waitcnt(kWaitVm | LOADS);
-    VSA_BARRIER();
-
-    // Block 1 (keys 32..63) is computed only if it holds valid keys; its
-    // registers are read only for chunks below nchunk.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (active && (b == 0 || nj > 32)) {
-        const char* krow = lds_k + (32 * b + l32) * KROWB;
-        if constexpr (QK8) {
-          // Scale bytes 127 (2^0): plain E4M3 x E4M3 products, fp32 sums.
-#pragma unroll
-          for (int m = 0; m < NK64; ++m) {
-            const int lc = 4 * m + 2 * hl;
-            const u32x4 k0 = *reinterpret_cast<const u32x4*>(krow + ((lc ^ kswz_r) << 4));
-            const u32x4 k1 = *reinterpret_cast<const u32x4*>(krow + (((lc + 1) ^ kswz_r) << 4));
-            const i32x8 kf = __builtin_bit_cast(
-                i32x8, u32x8{k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w});
-            sacc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                kf, qf8[m], m == 0 ? f32x16{} : sacc[b], 0, 0, 0, 127, 0, 127);
-          }
-          // Key dequantisation scales (before the pad mask: pad scales are 0).
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 ks = *reinterpret_cast<const f32x4*>(lds_k + K_TILE + 1024 * b +
-                                                             4 * (8 * r4 + 4 * hl));
-            sacc[b][4 * r4 + 0] *= ks.x;
-            sacc[b][4 * r4 + 1] *= ks.y;
-            sacc[b][4 * r4 + 2] *= ks.z;
-            sacc[b][4 * r4 + 3] *= ks.w;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < NCK; ++c) {
-            const bf16x8 kf =
-                *reinterpret_cast<const bf16x8*>(krow + (((2 * c + hl) ^ kswz_r) << 4));
-            sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c],
-                                                              c == 0 ? f32x16{} : sacc[b], 0, 0, 0);
-          }
-        }
-      }
-    }
-    VSA_BARRIER();  // every wave is done with K(t)
+    const bool has1 = nj > 32;   // the second half holds a valid key
     // The last iteration re-requests its own tile, so that every iteration
-    // issues the same loads and the wait counts below stay exact.
+    // issues the same loads and the wait counts stay exact.
     const int jn = it + 1 < end ? tile_at(it + 1) : j;
     const int njn = valid[jn];
-    const int kl_next = k_loads(njn);
-    VSA_LOAD_K(jn, kl_next);
 
-    // Lane holds keys 32b + 8(r/4) + 4hl + r%4 of query column l32; 16-key
-    // chunk e is registers 8(e%2)..8(e%2)+7 of block e/2.
-    if (active && (nj & 15)) {
-      // Key 32b + 8(r/4) + 4hl + r%4 is a pad key iff its constant part
-      // reaches nj - 4hl (one per-lane limit, not one index per register).
-      const int lim = nj - 4 * hl;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * b + 8 * (r >> 2) + (r & 3) >= lim) sacc[b][r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (e < nchunk) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sacc[e >> 1][8 * (e & 1) + r]);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) oacc[n] *= alpha;
-    }
-
-    bf16x8 pf[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (e < nchunk) {
-        float pv[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          pv[r] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 1][8 * (e & 1) + r], scale_log2, -m_run));
-          psum += pv[r];
-        }
-        u32x4 pu;
-        pu.x = pack_bf16x2(pv[0], pv[1]);
-        pu.y = pack_bf16x2(pv[2], pv[3]);
-        pu.z = pack_bf16x2(pv[4], pv[5]);
-        pu.w = pack_bf16x2(pv[6], pv[7]);
-        pf[e] = __builtin_bit_cast(bf16x8, pu);
-      }
-    }
-    l_run += psum;
-
-    // V(t) landed (the K(t+1) group may still be in flight).
-    switch (kl_next + (QK8 ? 1 : 0)) {
-      case 0: __builtin_amdgcn_s_waitcnt(kWaitVm | 0); break;
-      case 1: __builtin_amdgcn_s_waitcnt(kWaitVm | 1); break;
-      case 2: __builtin_amdgcn_s_waitcnt(kWaitVm | 2); break;
-      case 3: __builtin_amdgcn_s_waitcnt(kWaitVm | 3); break;
-      case 4: __builtin_amdgcn_s_waitcnt(kWaitVm | 4); break;
-      case 5: __builtin_amdgcn_s_waitcnt(kWaitVm | 5); break;
-      case 6: __builtin_amdgcn_s_waitcnt(kWaitVm | 6); break;
-      case 7: __builtin_amdgcn_s_waitcnt(kWaitVm | 7); break;
-      default: __builtin_amdgcn_s_waitcnt(kWaitVm | 8); break;
-    }
+    // K half 0 of t landed; every wave is done with V^T half 1 of t - 1.
+    wait_vm(ck(nj, 1) + cv(nj, 0));
     VSA_BARRIER();
+    if (has1) VSA_LOAD_VH(lds_vb, j, 1);
+
+    f32x16 s0, s1;
+    bf16x8 pf[4];
+    if (active) {
+      // Phase 1.
+      qk_phase(0, s0, false, kNone, 0.0f, pf[0], pf[1]);
+      if (nj < 32) mask_half(s0, 0, nj);
+      const float m0 = raised_max(max16(s0));
+      if (m0 != m_run) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m0);
+        m_run = m0;
+        l_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (e < nchunk) {
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          const char* vrow = lds_v + (32 * n + l32) * 128;
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + (((2 * e + hl) ^ vswz_r) << 4));
-          oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[e], oacc[n], 0, 0, 0);
-        }
+        for (int n = 0; n < NB; ++n) oacc[n] *= alpha;
       }
     }
-    VSA_BARRIER();  // every wave is done with V(t)
-    VSA_LOAD_V(vth + static_cast<size_t>(jn) * TILE_BYTES, njn);
+    // K half 1 of t landed; every wave is done with K half 0 of t.
+    wait_vm(cv(nj, 0) + cv(nj, 1));
+    VSA_BARRIER();
+    VSA_LOAD_KH(lds_ka, jn, 0);
+
+    float alpha1 = 1.0f;
+    if (active) {
+      // Phase 2 (the pinned copy keeps the softmax inside the branch).
+      if (has1) {
+        l_run += qk_phase(1, s1, true, s0, pinned(m_run), pf[0], pf[1]);
+      } else {
+        uint32_t pv[8];
+        float ps = 0.0f;
+        sm_part(0, 1, s0, m_run, pv, ps);
+        pack16(pv, pf[0], pf[1]);
+        l_run += ps;
+      }
+      // The second half's max is settled before P.V of the first half starts.
+      if (has1) {
+        if (nj < 64) mask_half(s1, 1, nj);
+        const float m1 = raised_max(max16(s1));
+        alpha1 = __builtin_amdgcn_exp2f(m_run - m1);
+        m_run = m1;
+      }
+    }
+    const bool resc1 = __builtin_amdgcn_ballot_w64(alpha1 != 1.0f) != 0;
+
+    // V^T half 0 of t landed; every wave is done with K half 1 of t.
+    wait_vm(cv(nj, 1) + ck(njn, 0));
+    VSA_BARRIER();
+    if (njn > 32) VSA_LOAD_KH(lds_kb, jn, 1);
+
+    if (active) {
+      if (has1) {
+        if (resc1) {
+          // Rare: the second half raised the max.  O, the row sum and the
+          // first half's probabilities (already bf16) move to the new max
+          // before they are combined, so O is only ever updated in place.
+          l_run *= alpha1;
+#pragma unroll
+          for (int n = 0; n < NB; ++n) oacc[n] *= alpha1;
+          rescale_bf16(pf[0], alpha1);
+          rescale_bf16(pf[1], alpha1);
+        }
+        // Phase 3.
+        l_run += pv_phase(0, pf[0], pf[1], true, s1, pinned(m_run), pf[2], pf[3]);
+      } else {
+        pv_phase(0, pf[0], pf[1], false, kNone, 0.0f, pf[2], pf[3]);
+      }
+    }
+    // V^T half 1 of t landed; every wave is done with V^T half 0 of t.
+    wait_vm(ck(njn, 0) + ck(njn, 1));
+    VSA_BARRIER();
+    VSA_LOAD_VH(lds_va, jn, 0);
+
+    if (active && has1) {
+      // Phase 4.
+      pv_phase(1, pf[2], pf[3], false, kNone, 0.0f, pf[2], pf[3]);
+    }
     j = jn;
     nj = njn;
   }
   // No global->LDS load may still be in flight when the block's LDS is released.
   __builtin_amdgcn_s_waitcnt(kWaitVm);
-#undef VSA_LOAD_K
-#undef VSA_LOAD_V
+#undef VSA_LOAD_KH
+#undef VSA_LOAD_VH
 #undef VSA_BARRIER
 
   if (!last) {

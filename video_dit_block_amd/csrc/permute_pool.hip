@@ -8,8 +8,9 @@
 // One block per (head, tile).  The tile's 64 slots of q, k and v are staged
 // in LDS (pad slots zero), then
 //   - k is written to Kt[h][tile][slot][d] (bf16),
-//   - v is written transposed to Vt[h][tile][d][pos] (bf16), the layout the
-//     fine kernel's P.V operand wants: inside each group of 16 slots the
+//   - v is written transposed to Vt[h][tile][half][d][pos] (bf16, positions
+//     0-31 and 32-63 in two halves, so that the fine kernel can fetch a half
+//     tile as one block), the layout its P.V operand wants: inside each group of 16 slots the
 //     storage order is slots 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the slot
 //     swapped), so that the 8 keys one MFMA lane contracts over are adjacent;
 //   - q, k, v are mean-pooled per channel: a sequential fp32 sum over the
@@ -219,8 +220,9 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
       *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
     }
   }
-  // Vt: [d][pos] bf16, 16-byte chunks of 8 positions.  Positions p0..p0+7
-  // (p0 = 8m) hold slots 16(m/2) + 4(m%2) + {0..3} and the same + 8.
+  // Vt: two halves of positions (0-31, 32-63), each [d][32] bf16 with
+  // 16-byte chunks of 8 positions.  Positions p0..p0+7 (p0 = 8m) hold slots
+  // 16(m/2) + 4(m%2) + {0..3} and the same + 8.
   {
     uint16_t* dst = vt + tile_base * 64 * D;
     for (int c = tid; c < D * 8; c += blockDim.x) {
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
       o.y = pack_bf16x2(to_f32(lds[2][sa + 2][d]), to_f32(lds[2][sa + 3][d]));
       o.z = pack_bf16x2(to_f32(lds[2][sb + 0][d]), to_f32(lds[2][sb + 1][d]));
       o.w = pack_bf16x2(to_f32(lds[2][sb + 2][d]), to_f32(lds[2][sb + 3][d]));
-      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(d) * 64 + 8 * m) = o;
+      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(m >> 2) * 32 * D + d * 32 + 8 * (m & 3)) = o;
     }
   }
 }
