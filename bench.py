@@ -93,6 +93,21 @@ def fine_flops(sel: np.ndarray, valid: np.ndarray, P: int, L: int, D: int) -> tu
     return alg, padded
 
 
+def kv_stream_bytes(sel: np.ndarray, valid: np.ndarray, P: int, D: int, qk_fp8: bool) -> float:
+    """Bytes of K and V^T the fine kernel streams from L2 into LDS in one
+    forward: every visit of key tile j brings its 32-key halves that hold a
+    valid key (one or two), each a K half (32 keys x D, bf16 or E4M3 codes
+    plus 32 fp32 scales) and a V^T half (D x 32 keys, bf16)."""
+    H, NV, topk = sel.shape
+    halves = 1.0 + (valid > 32)
+    kh = 32 * D * (1 if qk_fp8 else 2) + (32 * 4 if qk_fp8 else 0)
+    vh = 32 * D * 2
+    per_tile = halves * (kh + vh)
+    prefix_rows = P * float(per_tile.sum()) * H
+    video_rows = NV * H * float(per_tile[:P].sum()) + float(per_tile[sel].sum())
+    return prefix_rows + video_rows
+
+
 def sources_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -238,6 +253,8 @@ def main():
     sel_h = sel.cpu().numpy()
     alg_fine, padded_fine = fine_flops(sel_h.astype(np.int64), valid, plan.num_prefix_tiles,
                                        plan.L, w.head_dim)
+    kv_bytes = kv_stream_bytes(sel_h.astype(np.int64), valid, plan.num_prefix_tiles, w.head_dim,
+                               bool(args.qk_fp8))
     coarse_flops = 4.0 * w.head_dim * plan.num_tiles ** 2 * w.heads
     total = alg_fine + coarse_flops
     tflops = total / (ms_per_step * 1e-3) / 1e12
@@ -286,6 +303,10 @@ def main():
             "key_chunk_tiles": plan.chunk_tiles,
             "algorithmic_flops_per_launch": alg_fine / launches,
             "avg_launch_ms": round(fine_ms / launches, 4),
+            # The kernel's other ceiling: K/V bytes moved from L2 into LDS.
+            "kv_stream": {"bytes_per_launch": kv_bytes / launches,
+                          "achieved": round(kv_bytes / (fine_ms * 1e-3) / 1e12, 2),
+                          "unit": "TB/s"},
         },
     }
     if not args.no_cpu_baseline and not args.profile_pass and not args.qk_prep and not args.qk_fp8:
