@@ -321,7 +321,8 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   //   K half:   [KROWB/64 groups][32 keys][64 B]: chunks 4G..4G+3 of a key
   //             row; logical chunk c sits at (c ^ swz64(key)) in its group;
   //   V^T half: [D rows][64 B] (the 32 keys of the half), the same swizzle.
-  // DMA load number x (0..2*LOADS-1 over both waves, 64 lanes x 16 B each)
+  // DMA load number x (0..2*KH_LOADS-1, or 0..2*VH_LOADS-1, over both waves;
+  // 64 lanes x 16 B each)
   // fills LDS chunks 64x..64x+63: K rows 16(x % 2) + lane/4 of group x/2,
   // V^T rows 16x + lane/4.  The lane part of the source offset is the same
   // for every load, the rest is uniform.
