@@ -1,0 +1,67 @@
+"""Host-side accounting of bench.py (no GPU): the algorithmic fine-branch
+flops and the K/V bytes the fine kernel streams, each against a brute-force
+count over every (head, query tile, key tile) visit."""
+import numpy as np
+
+import bench
+import oracle
+from workloads import AUDIO, TEXT, Workload, make_layout
+
+
+def _geometry():
+    # 100 text tokens (one full and one partial prefix tile), a 6x10x10 grid:
+    # tiles of 4x4x4 with partial tiles along every axis
+    w = Workload("acct", 3, 64, "f32", ((TEXT, 100), (AUDIO, 40)), (6, 10, 10), 0.7)
+    tags, pos = make_layout(w)
+    g = oracle.geometry(tags, pos, w.grid)
+    return w, g
+
+
+def _random_selection(g, H, topk, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.stack([np.stack([np.sort(rng.choice(np.arange(g.P, g.Nt), topk, replace=False))
+                               for _ in range(g.NV)]) for _ in range(H)])
+
+
+def _visits(g, sel, h, i):
+    return list(range(g.Nt)) if i < g.P else list(range(g.P)) + [int(t) for t in sel[h, i - g.P]]
+
+
+def test_fine_flops_brute_force():
+    w, g = _geometry()
+    topk = oracle.topk_count(g.NV, w.sparsity)
+    sel = _random_selection(g, w.heads, topk)
+    alg, padded = bench.fine_flops(sel, g.valid, g.P, g.L, w.head_dim)
+    a = p = 0.0
+    for h in range(w.heads):
+        for i in range(g.Nt):
+            for j in _visits(g, sel, h, i):
+                a += 4.0 * w.head_dim * g.valid[i] * g.valid[j]
+                p += 4.0 * w.head_dim * 64 * 64
+    assert alg == a and padded == p
+
+
+def test_kv_stream_bytes_brute_force():
+    w, g = _geometry()
+    topk = oracle.topk_count(g.NV, w.sparsity)
+    sel = _random_selection(g, w.heads, topk, seed=1)
+    D = w.head_dim
+    for fp8 in (False, True):
+        got = bench.kv_stream_bytes(sel, g.valid, g.P, D, fp8)
+        want = 0
+        for h in range(w.heads):
+            for i in range(g.Nt):
+                for j in _visits(g, sel, h, i):
+                    halves = 2 if g.valid[j] > 32 else 1
+                    k_half = 32 * D * (1 if fp8 else 2) + (32 * 4 if fp8 else 0)
+                    want += halves * (k_half + 32 * D * 2)
+        assert got == want, (fp8, got, want)
+
+
+def test_kv_stream_counts_one_half_for_short_tiles():
+    w, g = _geometry()
+    assert (g.valid <= 32).any() and (g.valid > 32).any()
+    sel = _random_selection(g, w.heads, 1, seed=2)
+    full = bench.kv_stream_bytes(sel, np.full_like(g.valid, 64), g.P, w.head_dim, False)
+    part = bench.kv_stream_bytes(sel, g.valid, g.P, w.head_dim, False)
+    assert part < full
