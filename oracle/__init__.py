@@ -13,5 +13,6 @@ from .vsa_h3 import (  # noqa: F401
     Geometry, GeometryError, geometry, topk_count, to_f32, pool_canonical,
     scores_canonical, select_topk, key_tiles, fine_item, fine, coarse, combine,
     round_bf16_from_f64, forward, forward_head, qk_norm_rope, prep_qk, e4m3_encode,
+    ref_keep_count, select_ref,
     e4m3_decode, quantize_rows, dequantize_rows, E4M3_MAX,
 )

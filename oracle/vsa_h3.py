@@ -52,6 +52,23 @@ design notes of the repository):
   R13 all non-video tokens precede all video tokens; video positions are
      zero-based and cover the grid exactly once.
 
+Variant with 128-token tiles and a reference keep ratio (the OmniRef page,
+section "Device profiles": its Blackwell stack runs VSA at sparsity 0.9 with
+128-token tiles and reference keep 0.1; neither the tile shape nor the keep
+rule is spelled out there):
+  R22 a video tile is a (tt, ty, tx) box of 64 or 128 grid cells, given by
+     the caller; tiles cover the grid in (t/tt, y/ty, x/tx) raster order and
+     prefix tiles hold as many tokens as a video tile (R12 with that count).
+     The 128-token shape used by the workloads is (4, 8, 4), which divides the
+     height and width of the 480p and 768p grids;
+  R23 reference keep r in (0, 1]: a video query tile keeps only the
+     kr = max(1, min(ceil(r * NR), NR)) reference key tiles (tag cond, NR of
+     them) with the highest unscaled scores, ties to the lower tile index,
+     next to the top-k video tiles; text and audio key tiles stay always
+     visited, prefix query tiles stay dense, and the compression branch still
+     covers every key tile.  r = 1 keeps every reference tile, which is the
+     method without the keep ratio.
+
 Optional upstream step, fused into the tile gather ("FastH3 NVFP4 on RTX PRO
 6000", section "Model integration": QK-norm and RoPE are applied to the
 tile-ordered q and k with cos/sin tables computed once per step, and pad rows
@@ -96,6 +113,10 @@ something other than itself:
   scores_canonical   float64 dot product within the fp32 error bound;
                      constructed exact cases
   select_topk        exhaustive Python sort on (-score, index); forced ties
+  select_ref         exhaustive Python sort over the reference tiles only;
+                     r = 1 reproduces the unrestricted key lists
+  geometry (128)     closed-form tile counts and extents for (4, 8, 4) and
+                     (8, 4, 4) boxes; raster slot order; 128-token prefix cuts
   fine / fine_item   sparsity 0 == torch SDPA (float64) on the packed
                      sequence; prefix rows == dense rows at any sparsity;
                      token-level masked dense attention on tiny grids
@@ -130,6 +151,7 @@ import numpy as np
 TEXT, COND, AUDIO, VIDEO = 0, 1, 2, 3
 TILE_TOKENS = 64
 TILE_DIMS = (4, 4, 4)
+TILE_TOKEN_COUNTS = (64, 128)      # video tile volumes that are defined (R22)
 
 
 class GeometryError(ValueError):
@@ -144,10 +166,15 @@ class Geometry:
     tiles: list             # per tile: int64 array of packed indices in slot order
     tile_tag: np.ndarray    # [Nt] segment tag of each tile
     grid: tuple
+    tile_dims: tuple = TILE_DIMS
 
     @property
     def Nt(self) -> int:
         return self.P + self.NV
+
+    @property
+    def tile_tokens(self) -> int:
+        return int(np.prod(self.tile_dims))
 
     @property
     def valid(self) -> np.ndarray:
@@ -166,8 +193,8 @@ class Geometry:
         return out
 
     def perm(self) -> np.ndarray:
-        """[Nt, 64] packed index of each slot, -1 for pad slots."""
-        p = np.full((self.Nt, TILE_TOKENS), -1, dtype=np.int64)
+        """[Nt, tile_tokens] packed index of each slot, -1 for pad slots."""
+        p = np.full((self.Nt, self.tile_tokens), -1, dtype=np.int64)
         for j, idx in enumerate(self.tiles):
             p[j, :len(idx)] = idx
         return p
@@ -182,10 +209,21 @@ def topk_count(n_video_tiles: int, sparsity: float) -> int:
     return max(1, min(math.ceil((1.0 - s) * n_video_tiles), n_video_tiles))
 
 
+def ref_keep_count(n_ref_tiles: int, keep: float) -> int:
+    """Reference tiles kept per video query tile under keep ratio r (R23), in
+    IEEE double like the top-k rule."""
+    if n_ref_tiles <= 0:
+        return 0
+    return max(1, min(math.ceil(float(keep) * n_ref_tiles), n_ref_tiles))
+
+
 def geometry(token_tags, position_ids, grid, tile=TILE_DIMS) -> Geometry:
-    """Tile geometry from tags and positions (readings R9-R13)."""
-    if tuple(tile) != TILE_DIMS:
-        raise GeometryError("only (4, 4, 4) video tiles are defined")
+    """Tile geometry from tags and positions (readings R9-R13, R22)."""
+    tile = tuple(int(d) for d in tile)
+    if len(tile) != 3 or min(tile) < 1 or int(np.prod(tile)) not in TILE_TOKEN_COUNTS:
+        raise GeometryError("a video tile is a box of 64 or 128 grid cells")
+    tt, ty, tx = tile
+    n_tile = tt * ty * tx
     tags = np.asarray(token_tags, dtype=np.int64).reshape(-1)
     pos = np.asarray(position_ids, dtype=np.int64).reshape(-1, 3)
     L = tags.shape[0]
@@ -203,14 +241,14 @@ def geometry(token_tags, position_ids, grid, tile=TILE_DIMS) -> Geometry:
         raise GeometryError("video token count does not match the grid")
 
     tiles, tile_tag = [], []
-    # Prefix: maximal runs of one tag, cut into 64-token chunks in packed order.
+    # Prefix: maximal runs of one tag, cut into tile-sized chunks in packed order.
     start = 0
     while start < n_pre:
         end = start
         while end < n_pre and tags[end] == tags[start]:
             end += 1
-        for c in range(start, end, TILE_TOKENS):
-            tiles.append(np.arange(c, min(c + TILE_TOKENS, end), dtype=np.int64))
+        for c in range(start, end, n_tile):
+            tiles.append(np.arange(c, min(c + n_tile, end), dtype=np.int64))
             tile_tag.append(int(tags[start]))
         start = end
     P = len(tiles)
@@ -225,9 +263,9 @@ def geometry(token_tags, position_ids, grid, tile=TILE_DIMS) -> Geometry:
         cell = (t * H + y) * W + x
         if np.unique(cell).shape[0] != nvid:
             raise GeometryError("duplicate video position")
-        nt, nh, nw = -(-T // 4), -(-H // 4), -(-W // 4)
+        nt, nh, nw = -(-T // tt), -(-H // ty), -(-W // tx)
         NV = nt * nh * nw
-        vtile = ((t // 4) * nh + (y // 4)) * nw + (x // 4)
+        vtile = ((t // tt) * nh + (y // ty)) * nw + (x // tx)
         # order: by video tile, then (t, y, x) raster inside it
         order = np.lexsort((x, y, t, vtile))
         sorted_tile = vtile[order]
@@ -236,7 +274,7 @@ def geometry(token_tags, position_ids, grid, tile=TILE_DIMS) -> Geometry:
             tiles.append(vidx[order[bounds[j]:bounds[j + 1]]])
             tile_tag.append(VIDEO)
     return Geometry(L=L, P=P, NV=NV, tiles=tiles, tile_tag=np.array(tile_tag, np.int64),
-                    grid=(T, H, W))
+                    grid=(T, H, W), tile_dims=tile)
 
 
 def to_f32(x) -> np.ndarray:
@@ -263,7 +301,7 @@ def pool_canonical(x32: np.ndarray, geom: Geometry) -> np.ndarray:
     perm = geom.perm()
     n = geom.valid
     acc = np.zeros((geom.Nt, D), dtype=np.float32)
-    for s in range(TILE_TOKENS):
+    for s in range(geom.tile_tokens):
         live = np.nonzero(s < n)[0]
         if live.size == 0:
             break
@@ -295,20 +333,38 @@ def select_topk(S: np.ndarray, geom: Geometry, topk: int) -> np.ndarray:
     return (np.sort(order, axis=1) + P).astype(np.int32)
 
 
-def key_tiles(geom: Geometry, sel: np.ndarray, i: int) -> np.ndarray:
-    """Key tiles visited by query tile i: all tiles for a prefix query tile,
-    prefix tiles plus the selected video tiles for a video query tile."""
+def select_ref(S: np.ndarray, geom: Geometry, kr: int) -> np.ndarray:
+    """The kr reference key tiles (tag cond) of each video query tile with the
+    highest scores, ties to the lower index (R23), ascending.
+
+    Returns int32 [NV, kr] of global tile indices."""
+    ref = np.nonzero(geom.tile_tag == COND)[0]
+    if geom.NV == 0 or kr == 0:
+        return np.zeros((geom.NV, 0), dtype=np.int32)
+    rows = S[geom.P:][:, ref]
+    order = np.argsort(-rows, axis=1, kind="stable")[:, :kr]
+    return np.sort(ref[order], axis=1).astype(np.int32)
+
+
+def key_tiles(geom: Geometry, sel: np.ndarray, i: int, ref_sel=None) -> np.ndarray:
+    """Key tiles visited by query tile i: all tiles for a prefix query tile;
+    for a video query tile the prefix tiles (only the selected ones among the
+    reference tiles when ``ref_sel`` is given) plus the selected video tiles."""
     if i < geom.P:
         return np.arange(geom.Nt)
-    return np.concatenate([np.arange(geom.P), sel[i - geom.P].astype(np.int64)])
+    prefix = np.arange(geom.P)
+    if ref_sel is not None:
+        prefix = np.concatenate([prefix[geom.tile_tag[:geom.P] != COND],
+                                 ref_sel[i - geom.P].astype(np.int64)])
+    return np.concatenate([prefix, sel[i - geom.P].astype(np.int64)])
 
 
 def fine_item(q64: np.ndarray, k64: np.ndarray, v64: np.ndarray, geom: Geometry,
-              sel: np.ndarray, i: int, scale: float) -> np.ndarray:
+              sel: np.ndarray, i: int, scale: float, ref_sel=None) -> np.ndarray:
     """Softmax attention of query tile i's valid rows over the valid tokens of
     its key tiles (float64, one head).  Returns [n_i, D]."""
     rows = geom.tiles[i]
-    keys = np.concatenate([geom.tiles[j] for j in key_tiles(geom, sel, i)])
+    keys = np.concatenate([geom.tiles[j] for j in key_tiles(geom, sel, i, ref_sel)])
     logits = (q64[rows] @ k64[keys].T) * scale
     logits -= logits.max(axis=1, keepdims=True)
     p = np.exp(logits)
@@ -317,12 +373,12 @@ def fine_item(q64: np.ndarray, k64: np.ndarray, v64: np.ndarray, geom: Geometry,
 
 
 def fine(q64, k64, v64, geom: Geometry, sel: np.ndarray, scale: float,
-         items=None) -> np.ndarray:
+         items=None, ref_sel=None) -> np.ndarray:
     """Fine branch of one head for all query tiles (or ``items``): [L, D] float64,
     rows of tiles not computed are NaN."""
     out = np.full((geom.L, q64.shape[1]), np.nan)
     for i in (range(geom.Nt) if items is None else items):
-        out[geom.tiles[i]] = fine_item(q64, k64, v64, geom, sel, i, scale)
+        out[geom.tiles[i]] = fine_item(q64, k64, v64, geom, sel, i, scale, ref_sel)
     return out
 
 
@@ -443,12 +499,15 @@ class HeadResult:
     c: np.ndarray
     o: np.ndarray | None        # [L, D] float64 (NaN rows where not computed)
     out: np.ndarray | None      # [L, D] float64 before I/O rounding
+    ref_sel: np.ndarray | None = None   # [NV, kr] with a reference keep ratio below 1
 
 
 def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
-                 with_fine: bool = True, qk_fp8: bool = False) -> HeadResult:
+                 with_fine: bool = True, qk_fp8: bool = False,
+                 ref_keep: float = 1.0) -> HeadResult:
     """The whole forward for head h.  q, k, v, gate: [L, H, D] (torch or numpy).
-    qk_fp8: the fine branch uses per-token FP8 q and k (R19-R21)."""
+    qk_fp8: the fine branch uses per-token FP8 q and k (R19-R21).
+    ref_keep: reference keep ratio r of R23 (1 keeps every reference tile)."""
     qh = to_f32(q[:, h, :])
     kh = to_f32(k[:, h, :])
     vh = to_f32(v[:, h, :])
@@ -459,6 +518,12 @@ def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
     vp = pool_canonical(vh, geom)
     S = scores_canonical(qp, kp)
     sel = select_topk(S, geom, topk)
+    ref_sel = None
+    if not 0.0 < ref_keep <= 1.0:
+        raise ValueError("the reference keep ratio must lie in (0, 1]")
+    if ref_keep < 1.0:
+        ref_sel = select_ref(S, geom, ref_keep_count(int(np.sum(geom.tile_tag == COND)),
+                                                     ref_keep))
     c = coarse(S, vp, scale)
     o = out = None
     if with_fine:
@@ -467,9 +532,9 @@ def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
             k64 = dequantize_rows(*quantize_rows(kh))
         else:
             q64, k64 = qh.astype(np.float64), kh.astype(np.float64)
-        o = fine(q64, k64, vh.astype(np.float64), geom, sel, scale, items)
+        o = fine(q64, k64, vh.astype(np.float64), geom, sel, scale, items, ref_sel)
         out = combine(o, to_f32(gate[:, h, :]), c, geom)
-    return HeadResult(qp, kp, vp, S, sel, c, o, out)
+    return HeadResult(qp, kp, vp, S, sel, c, o, out, ref_sel)
 
 
 def prep_qk(q, k, q_weight, k_weight, eps, cos, sin):
@@ -490,7 +555,7 @@ def prep_qk(q, k, q_weight, k_weight, eps, cos, sin):
 
 
 def forward(q, k, v, gate, token_tags, position_ids, grid, sparsity, tile=TILE_DIMS,
-            heads=None):
+            heads=None, ref_keep: float = 1.0):
     """Whole VSA-H3 forward on all (or the listed) heads.
 
     Returns a dict with
@@ -507,7 +572,7 @@ def forward(q, k, v, gate, token_tags, position_ids, grid, sparsity, tile=TILE_D
     out = np.full((L, H, D), np.nan)
     res = {"geom": geom, "topk": topk, "heads": {}}
     for h in hs:
-        r = forward_head(q, k, v, gate, geom, topk, h)
+        r = forward_head(q, k, v, gate, geom, topk, h, ref_keep=ref_keep)
         out[:, h, :] = (round_bf16_from_f64(r.out) if is_bf16
                         else r.out.astype(np.float32).astype(np.float64))
         res["heads"][h] = r
