@@ -16,6 +16,12 @@
  * tile's rows, multiplied by a per-token gate with no activation, and added.
  * The output returns to packed order ("Model integration" on the same page).
  *
+ * The OmniRef page ("Device profiles") also runs VSA with 128-token tiles
+ * and a reference keep ratio; both are options here: a video tile may be any
+ * box of 128 grid cells (prefix tiles then hold 128 tokens), and with keep
+ * ratio r < 1 (vsa_h3_plan_set_ref_keep) each video query tile visits only
+ * its best-scoring reference (cond) key tiles among the prefix tiles.
+ *
  * Conventions shared by every entry point
  *   - Every call returns a vsa_status; on failure vsa_h3_last_error() holds a
  *     message (thread-local, valid until the next call on the same thread).
@@ -68,37 +74,53 @@ typedef struct {
   uint64_t workspace_bytes;  /* bytes the workspace must hold */
   int32_t chunk_tiles;       /* key tiles per fine-branch key chunk */
   int32_t num_chunks;        /* key chunks, ceil(num_tiles / chunk_tiles); 0 if num_tiles == 0 */
+  int64_t num_ref_tiles;     /* prefix tiles of tag cond (reference tiles) */
+  int64_t topk_ref;          /* reference tiles kept per video query tile by the selection;
+                                0 when the keep ratio is 1 (every reference tile visited) */
+  double ref_keep;           /* reference keep ratio, 1 by default */
+  int32_t tile_tokens;       /* tokens per tile: 64 or 128 */
+  int32_t num_blocks;        /* 64-slot blocks, num_tiles * tile_tokens / 64 */
 } vsa_h3_info;
 
 /* Byte offsets of the intermediates inside the workspace (each 256-aligned).
  * They are documented so that tests and tools can read intermediates back;
- * their contents are only meaningful after a forward on the same stream. */
+ * their contents are only meaningful after a forward on the same stream.
+ * Token-level regions are laid out in 64-slot blocks: Nb = num_blocks blocks,
+ * one per 64-token tile, or two per 128-token tile (slots 0-63, then 64-127). */
 typedef struct {
-  uint64_t perm;    /* int32 [Nt][64]: packed row of each tile slot, -1 for pad slots */
-  uint64_t valid;   /* int32 [Nt]: valid tokens per tile */
-  uint64_t kt;      /* bf16 [H][Nt][64][D]: keys in tile order, pad rows zero */
-  uint64_t vt;      /* bf16 [H][Nt][2][D][32]: values in tile order, transposed, in two halves
-                       of 32 slots (0-31, 32-63), pad columns zero; inside each 16-slot
-                       group the columns hold slots 0-3, 8-11, 4-7, 12-15 */
+  uint64_t perm;    /* int32 [Nb][64]: packed row of each slot, -1 for pad slots */
+  uint64_t valid;   /* int32 [Nb]: valid tokens per block */
+  uint64_t kt;      /* bf16 [H][Nb][64][D]: keys in tile order, pad rows zero */
+  uint64_t vt;      /* bf16 [H][Nb][2][D][32]: values in tile order, transposed, in two halves
+                       of 32 slots (0-31, 32-63) per block, pad columns zero; inside each
+                       16-slot group the columns hold slots 0-3, 8-11, 4-7, 12-15 */
   uint64_t qp;      /* fp32 [H][Nt][D]: pooled (mean) q per tile */
   uint64_t kp;      /* fp32 [H][Nt][D]: pooled k */
   uint64_t vp;      /* fp32 [H][Nt][D]: pooled v */
   uint64_t scores;  /* fp32 [H][Nt][Ns]: tile scores, Ns = Nt rounded up to 4; after the
                        forward each row holds softmax(scores / sqrt(D)) instead */
   uint64_t coarse;  /* fp32 [H][Nt][D]: compression output per query tile */
-  uint64_t sel;     /* int32 [H][NV][topk]: selected video key tiles, ascending */
+  uint64_t sel;     /* int32 [H][NV][topk_ref + topk]: selected key tiles, ascending (the
+                       selected reference tiles, then the selected video tiles) */
   uint64_t total;   /* == vsa_h3_info.workspace_bytes */
   int64_t scores_row_stride;  /* Ns */
   uint64_t chunk_offsets;  /* int32 [H][NV][num_chunks + 1] (only if num_chunks > 1): entry c
-                              counts the selected tiles of the row with id < c * chunk_tiles */
+                              counts the listed tiles of the row with id < c * chunk_tiles (the
+                              selected video tiles, or with topk_ref > 0 the visit list) */
   uint64_t state;   /* fp32 fine-branch state between key chunks (only if num_chunks > 1);
                        internal layout */
-  uint64_t qt;      /* bf16 [H][Nt][64][D]: q after QK-norm + RoPE, tile order, pad rows zero
+  uint64_t qt;      /* bf16 [H][Nb][64][D]: q after QK-norm + RoPE, tile order, pad rows zero
                        (only with vsa_h3_plan_set_qk_prep) */
-  uint64_t kt8;     /* uint8 [H][Nt][64][D]: keys as OCP E4M3 codes, tile order, pad rows zero
+  uint64_t kt8;     /* uint8 [H][Nb][64][D]: keys as OCP E4M3 codes, tile order, pad rows zero
                        (only with vsa_h3_plan_set_qk_fp8) */
-  uint64_t kscale;  /* fp32 [H][Nt][64]: per-key dequantisation scale amax/448, pad slots zero
+  uint64_t kscale;  /* fp32 [H][Nb][64]: per-key dequantisation scale amax/448, pad slots zero
                        (only with vsa_h3_plan_set_qk_fp8) */
+  uint64_t kind;    /* int32 [Nt]: 0 prefix tile visited by every query, 1 reference (cond)
+                       tile, 2 video tile */
+  uint64_t visit;   /* int32 [H][NV][V] (only if topk_ref > 0): every key tile a video query
+                       tile visits, ascending: the non-reference prefix tiles, the selected
+                       reference tiles and the selected video tiles,
+                       V = (num_prefix_tiles - num_ref_tiles) + topk_ref + topk */
 } vsa_h3_ws_layout;
 
 /* Top-k rule of VSA-H3 evaluated in IEEE double as written; 0 when
@@ -114,12 +136,15 @@ int64_t vsa_h3_topk(int64_t num_video_tiles, double sparsity);
  *                 tokens only, which must cover grid exactly once.
  *   grid          post-patchify video grid (T, H, W); T*H*W must equal the
  *                 number of video tokens.
- *   tile          must be (4,4,4).
+ *   tile          (tt, th, tw) >= 1 with tt*th*tw = 64 (the pages' (4,4,4)) or
+ *                 128 (the OmniRef page's 128-token tiles; the pages do not
+ *                 give the box, (4,8,4) divides the 480p and 768p grids).
+ *                 Prefix tiles hold tt*th*tw tokens.
  *   heads >= 1; head_dim 64 or 128; sparsity in [0, 1].
- * Video tile of (t,y,x): P + ((t/4)*ceil(H/4) + y/4)*ceil(W/4) + x/4; slot
- * order inside a tile is the (t,y,x) raster of its valid cells.  Edge tiles
- * may be partial.  On success *plan_out owns host memory until
- * vsa_h3_plan_destroy. */
+ * Video tile of (t,y,x): P + ((t/tt)*ceil(H/th) + y/th)*ceil(W/tw) + x/tw;
+ * slot order inside a tile is the (t,y,x) raster of its valid cells.  Edge
+ * tiles may be partial.  VSA_E_UNSUPPORTED for another tile volume.  On
+ * success *plan_out owns host memory until vsa_h3_plan_destroy. */
 vsa_status vsa_h3_plan_create(const int64_t* token_tags, const int64_t* position_ids,
                               int64_t L, vsa_dims3 grid, vsa_dims3 tile, int32_t heads,
                               int32_t head_dim, double sparsity, vsa_h3_plan** plan_out);
@@ -143,8 +168,8 @@ vsa_status vsa_h3_plan_set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles);
 vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out);
 
 /* Host copies of the plan tables into caller-provided host buffers (any may
- * be NULL): perm int32 [Nt*64], valid int32 [Nt], tile_slot int32 [L] (tile*64
- * + slot of each packed token). */
+ * be NULL): perm int32 [Nt*tile_tokens], valid int32 [Nt] (tokens per tile),
+ * tile_slot int32 [L] (tile*tile_tokens + slot of each packed token). */
 vsa_status vsa_h3_plan_tables(const vsa_h3_plan* plan, int32_t* perm, int32_t* valid,
                               int32_t* tile_slot);
 
@@ -159,9 +184,11 @@ vsa_status vsa_h3_plan_upload(const vsa_h3_plan* plan, void* workspace,
  *   out            device [L][heads][head_dim] of io_dtype, fully written.
  *                  out = o_fine + gate * c[tile of the token], rounded to
  *                  io_dtype (nearest even).  Must not alias the inputs.
- *   sel_idx        device int32 [heads][NV][topk] or NULL; receives the
- *                  selected video key tiles (global tile ids, ascending).
- *                  NULL keeps them in the workspace only.
+ *   sel_idx        device int32 [heads][NV][topk_ref + topk] or NULL;
+ *                  receives the selected key tiles of each video query tile
+ *                  (global tile ids, ascending: the selected reference tiles
+ *                  when topk_ref > 0, then the selected video tiles).  NULL
+ *                  keeps them in the workspace only.
  *   workspace      device, 256-byte aligned, >= workspace_bytes, holding the
  *                  tables from vsa_h3_plan_upload.  Calls that overlap in
  *                  time must use different workspaces.
@@ -247,6 +274,21 @@ vsa_status vsa_h3_forward_qk_prep(const vsa_h3_plan* plan, const void* q, const 
  * The workspace size changes (regions kt8 and kscale): call before sizing and
  * uploading a workspace; 0 switches back to bf16 q and k. */
 vsa_status vsa_h3_plan_set_qk_fp8(vsa_h3_plan* plan, int32_t enable);
+
+/* Reference keep ratio (the OmniRef page, "Device profiles": its Blackwell
+ * stack keeps 0.1 of the reference tiles; the rule is not spelled out there).
+ * With keep r < 1 every video query tile of every later forward of this plan
+ * visits, among the prefix key tiles, the non-reference ones (text, audio)
+ * and only the
+ *     topk_ref = max(1, min(ceil(r * n_ref), n_ref))
+ * reference (cond) tiles with the highest tile scores (ties to the lower
+ * tile id; evaluated in IEEE double as written), next to its top-k video
+ * tiles.  Prefix query tiles still visit every tile, and the compression
+ * branch still covers every key tile.  r = 1 (the default) visits every
+ * reference tile.  The workspace size changes (sel width and the visit
+ * list): call before sizing and uploading a workspace.
+ * VSA_E_ARG if r is outside (0, 1] or NaN. */
+vsa_status vsa_h3_plan_set_ref_keep(vsa_h3_plan* plan, double keep);
 
 void vsa_h3_plan_destroy(vsa_h3_plan* plan);
 const char* vsa_h3_last_error(void);

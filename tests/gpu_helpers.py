@@ -32,13 +32,14 @@ def to_dev(x, dev="cuda"):
     return {k: (v.to(dev) if k in ("q", "k", "v", "gate") else v) for k, v in x.items()}
 
 
-def run(x, grid, sparsity, dev="cuda", plan=None, qk_fp8=False, chunk_tiles=0):
+def run(x, grid, sparsity, dev="cuda", plan=None, qk_fp8=False, chunk_tiles=0,
+        tile=(4, 4, 4), ref_keep=1.0):
     """GPU forward through the C ABI.  Returns (out, sel, plan, workspace)."""
     xd = {k: x[k].to(dev) for k in ("q", "k", "v", "gate")}
     L, H, D = xd["q"].shape
     if plan is None:
-        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity,
-                        chunk_tiles=chunk_tiles, qk_fp8=qk_fp8)
+        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity, tile,
+                        chunk_tiles=chunk_tiles, qk_fp8=qk_fp8, ref_keep=ref_keep)
     out, sel = vsa.forward(xd["q"], xd["k"], xd["v"], xd["gate"], plan=plan, return_sel=True)
     torch.cuda.synchronize()
     ws = plan.workspace(xd["q"].device)
@@ -68,15 +69,16 @@ def oracle_prep(x, prep):
 
 
 def intermediates(plan, ws):
-    H, D, Nt = plan.heads, plan.head_dim, plan.num_tiles
+    """Workspace regions on the host; kt and vt are per 64-slot block."""
+    H, D, Nt, Nb = plan.heads, plan.head_dim, plan.num_tiles, plan.num_blocks
     ns = plan.layout.scores_row_stride
     return {
         "qp": plan.view(ws, "qp", torch.float32, (H, Nt, D)).cpu().numpy(),
         "kp": plan.view(ws, "kp", torch.float32, (H, Nt, D)).cpu().numpy(),
         "vp": plan.view(ws, "vp", torch.float32, (H, Nt, D)).cpu().numpy(),
         "coarse": plan.view(ws, "coarse", torch.float32, (H, Nt, D)).cpu().numpy(),
-        "kt": plan.view(ws, "kt", torch.int16, (H, Nt, 64, D)).cpu(),
-        "vt": plan.view(ws, "vt", torch.int16, (H, Nt, 2, D, 32)).cpu(),
+        "kt": plan.view(ws, "kt", torch.int16, (H, Nb, 64, D)).cpu(),
+        "vt": plan.view(ws, "vt", torch.int16, (H, Nb, 2, D, 32)).cpu(),
         "probs": plan.view(ws, "scores", torch.float32, (H, Nt, ns)).cpu().numpy()[:, :, :Nt],
     }
 

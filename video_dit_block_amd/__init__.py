@@ -4,9 +4,11 @@ Video Sparse Attention as used by the FastH3 / MiniMax-H3 video DiT: packed
 [text | cond | audio | video] tokens are cut into 64-token tiles, a coarse
 branch scores mean-pooled tiles and produces a gated compression output, each
 video query tile keeps its top-k video key tiles (plus every prefix tile), and
-a block-sparse flash attention computes the fine branch.  All of it runs in
-hand-written HIP kernels behind the C ABI of ``include/vsa_h3.h``; this module
-only marshals arguments (PyTorch provides device memory and the stream).
+a block-sparse flash attention computes the fine branch.  The OmniRef variant
+(128-token tiles, a reference keep ratio for the cond tiles) is a plan option.
+All of it runs in hand-written HIP kernels behind the C ABI of
+``include/vsa_h3.h``; this module only marshals arguments (PyTorch provides
+device memory and the stream).
 
     import video_dit_block_amd as vsa
     out = vsa.forward(q, k, v, gate, token_tags, position_ids, grid=(T, H, W),
@@ -27,7 +29,7 @@ from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
     vsa_h3_oneshot_workspace_bytes, vsa_h3_plan_create, vsa_h3_plan_destroy, vsa_h3_plan_info,
     vsa_h3_plan_layout, vsa_h3_plan_set_chunk_tiles, vsa_h3_plan_tables, vsa_h3_plan_upload,
     vsa_h3_topk, vsa_h3_version, vsa_h3_plan_set_qk_prep, vsa_h3_forward_qk_prep,
-    vsa_h3_plan_set_qk_fp8,
+    vsa_h3_plan_set_qk_fp8, vsa_h3_plan_set_ref_keep,
 )
 
 __all__ = ["Plan", "forward", "forward_qk_prep", "VsaError", "vsa_h3_topk",
@@ -49,7 +51,7 @@ class Plan:
 
     def __init__(self, token_tags, position_ids, grid, heads, head_dim, sparsity,
                  tile=(4, 4, 4), chunk_tiles: int = 0, qk_prep: bool = False,
-                 qk_fp8: bool = False):
+                 qk_fp8: bool = False, ref_keep: float = 1.0):
         self.token_tags = _host_i64(token_tags).reshape(-1)
         self.position_ids = _host_i64(position_ids).reshape(-1, 3)
         self.grid = tuple(int(g) for g in grid)
@@ -65,6 +67,9 @@ class Plan:
         if qk_fp8:
             vsa_h3_plan_set_qk_fp8(self.handle, True)
         self.qk_fp8 = bool(qk_fp8)
+        if ref_keep != 1.0:
+            vsa_h3_plan_set_ref_keep(self.handle, ref_keep)
+        self.ref_keep = float(ref_keep)
         self.info = vsa_h3_plan_info(self.handle)
         self.layout = vsa_h3_plan_layout(self.handle)
         self._ws = {}
@@ -86,6 +91,16 @@ class Plan:
     @property
     def topk(self): return self.info.topk
     @property
+    def topk_ref(self): return self.info.topk_ref
+    @property
+    def num_ref_tiles(self): return self.info.num_ref_tiles
+    @property
+    def sel_width(self): return self.info.topk_ref + self.info.topk
+    @property
+    def tile_tokens(self): return self.info.tile_tokens
+    @property
+    def num_blocks(self): return self.info.num_blocks
+    @property
     def workspace_bytes(self): return self.info.workspace_bytes
     @property
     def chunk_tiles(self): return self.info.chunk_tiles
@@ -93,7 +108,7 @@ class Plan:
     def num_chunks(self): return self.info.num_chunks
 
     def tables(self):
-        """(perm [Nt, 64], valid [Nt], tile_slot [L]) as host int32 arrays."""
+        """(perm [Nt, tile_tokens], valid [Nt], tile_slot [L]) as host int32 arrays."""
         return vsa_h3_plan_tables(self.handle)
 
     def workspace(self, device, stream=None):
@@ -135,19 +150,20 @@ _plans_lock = threading.Lock()
 
 
 def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4, 4, 4),
-             qk_prep: bool = False) -> Plan:
+             qk_prep: bool = False, ref_keep: float = 1.0) -> Plan:
     """Cached Plan for this exact layout (keyed by a digest of tags and positions)."""
     tags = _host_i64(token_tags).reshape(-1)
     pos = _host_i64(position_ids).reshape(-1, 3)
     digest = hashlib.sha256(tags.tobytes() + b"|" + pos.tobytes()).hexdigest()
     key = (digest, tuple(grid), tuple(tile), int(heads), int(head_dim), float(sparsity),
-           bool(qk_prep))
+           bool(qk_prep), float(ref_keep))
     with _plans_lock:
         p = _plans.get(key)
         if p is not None:
             _plans.move_to_end(key)
             return p
-    p = Plan(tags, pos, grid, heads, head_dim, sparsity, tile, qk_prep=qk_prep)
+    p = Plan(tags, pos, grid, heads, head_dim, sparsity, tile, qk_prep=qk_prep,
+             ref_keep=ref_keep)
     with _plans_lock:
         _plans[key] = p
         while len(_plans) > 8:
@@ -156,10 +172,13 @@ def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4,
 
 
 def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsity=None,
-            tile=(4, 4, 4), *, plan: Plan | None = None, out=None, return_sel: bool = False):
+            tile=(4, 4, 4), *, ref_keep: float = 1.0, plan: Plan | None = None, out=None,
+            return_sel: bool = False):
     """VSA-H3 forward.  q, k, v, gate: CUDA tensors [L, heads, head_dim], contiguous,
-    all bfloat16 or all float32.  Returns out (same shape and dtype), and the
-    selected video key tiles int32 [heads, NV, topk] if ``return_sel``."""
+    all bfloat16 or all float32.  ``tile`` is the video tile box (64 or 128 grid
+    cells) and ``ref_keep`` the reference keep ratio (1 visits every reference
+    tile).  Returns out (same shape and dtype), and the selected key tiles
+    int32 [heads, NV, topk_ref + topk] if ``return_sel``."""
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda and gate.is_cuda):
         raise VsaError(-1, "q, k, v and gate must be GPU tensors (there is no CPU path)")
@@ -178,7 +197,7 @@ def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsi
             raise VsaError(-1, "tensors must be contiguous")
     L, H, D = q.shape
     if plan is None:
-        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile)
+        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile, ref_keep=ref_keep)
     if (plan.L, plan.heads, plan.head_dim) != (L, H, D):
         raise VsaError(-1, "plan does not match the tensors' [L, heads, head_dim]")
     dev = q.device
@@ -188,7 +207,8 @@ def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsi
         out = torch.empty_like(q)
     sel = None
     if return_sel:
-        sel = torch.empty((H, plan.num_video_tiles, plan.topk), dtype=torch.int32, device=dev)
+        sel = torch.empty((H, plan.num_video_tiles, plan.sel_width), dtype=torch.int32,
+                          device=dev)
     vsa_h3_forward(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), io,
                    out.data_ptr(), sel.data_ptr() if sel is not None and sel.numel() else None,
                    ws.data_ptr(), plan.workspace_bytes, stream)
@@ -197,8 +217,8 @@ def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsi
 
 def forward_qk_prep(q, k, v, gate, q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin,
                     token_tags=None, position_ids=None, grid=None, sparsity=None,
-                    tile=(4, 4, 4), *, plan: Plan | None = None, out=None,
-                    return_sel: bool = False):
+                    tile=(4, 4, 4), *, ref_keep: float = 1.0, plan: Plan | None = None,
+                    out=None, return_sel: bool = False):
     """VSA-H3 forward with QK RMS norm and RoPE applied to q and k while they
     are gathered into tile order.  q, k, v, gate as for ``forward`` (q and k
     before the norm); q_norm_weight, k_norm_weight: float32 CUDA [head_dim];
@@ -224,7 +244,8 @@ def forward_qk_prep(q, k, v, gate, q_norm_weight, k_norm_weight, eps, rope_cos, 
         if not t.is_contiguous():
             raise VsaError(-1, "tensors must be contiguous")
     if plan is None:
-        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile, qk_prep=True)
+        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile, qk_prep=True,
+                        ref_keep=ref_keep)
     if not plan.qk_prep:
         raise VsaError(-1, "plan was built without qk_prep=True")
     if (plan.L, plan.heads, plan.head_dim) != (L, H, D):
@@ -236,7 +257,8 @@ def forward_qk_prep(q, k, v, gate, q_norm_weight, k_norm_weight, eps, rope_cos, 
         out = torch.empty_like(q)
     sel = None
     if return_sel:
-        sel = torch.empty((H, plan.num_video_tiles, plan.topk), dtype=torch.int32, device=dev)
+        sel = torch.empty((H, plan.num_video_tiles, plan.sel_width), dtype=torch.int32,
+                          device=dev)
     vsa_h3_forward_qk_prep(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                            gate.data_ptr(), q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
                            float(eps), rope_cos.data_ptr(), rope_sin.data_ptr(), io,

@@ -26,7 +26,7 @@ EXPORTED = (
     "vsa_h3_plan_tables", "vsa_h3_plan_upload", "vsa_h3_forward", "vsa_h3_forward_timed",
     "vsa_h3_oneshot_workspace_bytes", "vsa_h3_forward_oneshot", "vsa_h3_plan_destroy",
     "vsa_h3_last_error", "vsa_h3_version", "vsa_h3_plan_set_qk_prep", "vsa_h3_forward_qk_prep",
-    "vsa_h3_plan_set_qk_fp8",
+    "vsa_h3_plan_set_qk_fp8", "vsa_h3_plan_set_ref_keep",
 )
 
 
@@ -45,7 +45,10 @@ class Info(ctypes.Structure):
                 ("num_video_tiles", ctypes.c_int64), ("num_tiles", ctypes.c_int64),
                 ("topk", ctypes.c_int64), ("heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
-                ("chunk_tiles", ctypes.c_int32), ("num_chunks", ctypes.c_int32)]
+                ("chunk_tiles", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("num_ref_tiles", ctypes.c_int64), ("topk_ref", ctypes.c_int64),
+                ("ref_keep", ctypes.c_double), ("tile_tokens", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32)]
 
 
 class WsLayout(ctypes.Structure):
@@ -53,7 +56,8 @@ class WsLayout(ctypes.Structure):
                                                "scores", "coarse", "sel", "total")] + \
                [("scores_row_stride", ctypes.c_int64), ("chunk_offsets", ctypes.c_uint64),
                 ("state", ctypes.c_uint64), ("qt", ctypes.c_uint64), ("kt8", ctypes.c_uint64),
-                ("kscale", ctypes.c_uint64)]
+                ("kscale", ctypes.c_uint64), ("kind", ctypes.c_uint64),
+                ("visit", ctypes.c_uint64)]
 
 
 _lib = None
@@ -99,6 +103,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_uint64, _P]
         L.vsa_h3_plan_set_qk_prep.argtypes = [_P, ctypes.c_int32]
         L.vsa_h3_plan_set_qk_fp8.argtypes = [_P, ctypes.c_int32]
+        L.vsa_h3_plan_set_ref_keep.argtypes = [_P, ctypes.c_double]
         L.vsa_h3_forward_qk_prep.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                              ctypes.c_int, _P, _P, _P, ctypes.c_uint64, _P,
                                              ctypes.POINTER(_P)]
@@ -162,9 +167,9 @@ def vsa_h3_plan_layout(plan: int) -> WsLayout:
 
 
 def vsa_h3_plan_tables(plan: int):
-    """Host copies: perm int32 [Nt, 64], valid int32 [Nt], tile_slot int32 [L]."""
+    """Host copies: perm int32 [Nt, tile_tokens], valid int32 [Nt], tile_slot int32 [L]."""
     info = vsa_h3_plan_info(plan)
-    perm = np.empty((info.num_tiles, 64), np.int32)
+    perm = np.empty((info.num_tiles, info.tile_tokens), np.int32)
     valid = np.empty(info.num_tiles, np.int32)
     ts = np.empty(info.L, np.int32)
     check(lib().vsa_h3_plan_tables(plan, perm.ctypes.data_as(_I32P), valid.ctypes.data_as(_I32P),
@@ -198,6 +203,10 @@ def vsa_h3_plan_set_qk_prep(plan: int, enable: bool) -> None:
 
 def vsa_h3_plan_set_qk_fp8(plan: int, enable: bool) -> None:
     check(lib().vsa_h3_plan_set_qk_fp8(plan, 1 if enable else 0))
+
+
+def vsa_h3_plan_set_ref_keep(plan: int, keep: float) -> None:
+    check(lib().vsa_h3_plan_set_ref_keep(plan, float(keep)))
 
 
 def vsa_h3_forward_qk_prep(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr: int,

@@ -15,6 +15,8 @@
 
 using vsa::set_error;
 
+static_assert(vsa::kKindRef == vsa::kKindRefTile, "reference tiles carry one kind value");
+
 namespace {
 
 vsa_status hip_fail(const char* what, hipError_t err) {
@@ -128,6 +130,11 @@ vsa_status vsa_h3_plan_info(const vsa_h3_plan* plan, vsa_h3_info* out) {
   out->workspace_bytes = plan->layout.total;
   out->chunk_tiles = plan->chunk_tiles;
   out->num_chunks = plan->num_chunks;
+  out->num_ref_tiles = plan->num_ref;
+  out->topk_ref = plan->topk_ref;
+  out->ref_keep = plan->ref_keep;
+  out->tile_tokens = plan->tile_tokens;
+  out->num_blocks = static_cast<int32_t>(plan->Nb);
   return VSA_OK;
 }
 
@@ -162,6 +169,8 @@ vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out) {
   out->qt = lo.qt;
   out->kt8 = lo.kt8;
   out->kscale = lo.kscale;
+  out->kind = lo.kind;
+  out->visit = lo.visit;
   return VSA_OK;
 }
 
@@ -192,9 +201,12 @@ vsa_status vsa_h3_plan_upload(const vsa_h3_plan* plan, void* workspace, uint64_t
   hipError_t err = hipMemcpyAsync(ws + plan->layout.perm, plan->perm.data(),
                                   plan->perm.size() * sizeof(int32_t), hipMemcpyHostToDevice, s);
   if (err != hipSuccess) return hip_fail("hipMemcpyAsync(perm)", err);
-  err = hipMemcpyAsync(ws + plan->layout.valid, plan->valid.data(),
-                       plan->valid.size() * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  err = hipMemcpyAsync(ws + plan->layout.valid, plan->bvalid.data(),
+                       plan->bvalid.size() * sizeof(int32_t), hipMemcpyHostToDevice, s);
   if (err != hipSuccess) return hip_fail("hipMemcpyAsync(valid)", err);
+  err = hipMemcpyAsync(ws + plan->layout.kind, plan->kind.data(),
+                       plan->kind.size() * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (err != hipSuccess) return hip_fail("hipMemcpyAsync(kind)", err);
   return VSA_OK;
 }
 
@@ -253,6 +265,8 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
   const int H = plan->heads, D = plan->head_dim;
   const int Nt = static_cast<int>(plan->Nt), P = static_cast<int>(plan->P);
   const int NV = static_cast<int>(plan->NV), topk = static_cast<int>(plan->topk);
+  const int topk_ref = static_cast<int>(plan->topk_ref), bsh = plan->bsh;
+  const int visit_len = static_cast<int>(vsa::visit_len(plan));
   const int32_t* perm = reinterpret_cast<const int32_t*>(ws + lo.perm);
   const int32_t* valid = reinterpret_cast<const int32_t*>(ws + lo.valid);
   uint16_t* kt = reinterpret_cast<uint16_t*>(ws + lo.kt);
@@ -279,20 +293,27 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
   }
   uint8_t* kt8 = plan->qk_fp8 ? reinterpret_cast<uint8_t*>(ws + lo.kt8) : nullptr;
   float* kscale = plan->qk_fp8 ? reinterpret_cast<float*>(ws + lo.kscale) : nullptr;
-  vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, kt, vt, qp, kp, vp, pp, kt8,
+  vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, bsh, kt, vt, qp, kp, vp, pp, kt8,
                           kscale};
   err = vsa::launch_permute_pool(pa, s);
   if (err != hipSuccess) return hip_fail("permute_pool launch", err);
   if ((err = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
+  int32_t* visit = topk_ref > 0 ? reinterpret_cast<int32_t*>(ws + lo.visit) : nullptr;
+  const int32_t* kind = reinterpret_cast<const int32_t*>(ws + lo.kind);
   vsa::CoarseArgs ca{qp, kp, vp, scores, coarse, sel, choff, H, Nt, static_cast<int>(lo.ns),
-                     P, NV, topk, D, nchunks, chunk_tiles};
+                     P, NV, topk, D, nchunks, chunk_tiles, kind, topk_ref, visit, visit_len};
   err = vsa::launch_coarse(ca, s);
   if (err != hipSuccess) return hip_fail("coarse launch", err);
   if ((err = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
-  vsa::FineArgs fa{q, pp.qt, gate, out, f32, kt, vt, coarse, perm, valid, sel, choff, state,
-                   H, Nt, P, NV, topk, D, nchunks, chunk_tiles, kt8, kscale};
+  // With a reference selection every key tile of a video query comes from
+  // its visit list; otherwise the prefix tiles are implicit and sel follows.
+  const int32_t* list = topk_ref > 0 ? visit : sel;
+  const int listlen = topk_ref > 0 ? visit_len : topk;
+  const int pvis = topk_ref > 0 ? 0 : P;
+  vsa::FineArgs fa{q, pp.qt, gate, out, f32, kt, vt, coarse, perm, valid, list, choff, state,
+                   H, Nt, P, NV, listlen, D, nchunks, chunk_tiles, kt8, kscale, bsh, pvis};
   err = vsa::launch_fine(fa, s);
   if (err != hipSuccess) return hip_fail("fine_attn launch", err);
   if ((err = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", err);
@@ -327,6 +348,14 @@ vsa_status vsa_h3_plan_set_qk_fp8(vsa_h3_plan* plan, int32_t enable) {
   }
   vsa::set_qk_fp8(plan, enable != 0);
   return VSA_OK;
+}
+
+vsa_status vsa_h3_plan_set_ref_keep(vsa_h3_plan* plan, double keep) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return VSA_E_ARG;
+  }
+  return vsa::set_ref_keep(plan, keep);
 }
 
 vsa_status vsa_h3_forward_qk_prep(const vsa_h3_plan* plan, const void* q, const void* k,

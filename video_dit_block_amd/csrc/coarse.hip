@@ -1,7 +1,9 @@
 // Coarse branch and top-k selection of VSA-H3 (FastH3 4-step Preview (VSA,
 // data-free), section "Video Sparse Attention is not optional here"):
 //   S[h][i][j]  = pooled q_i . pooled k_j in fp32           (tile scores)
-//   sel[h][i]   = top-k video key tiles of video query tile i by S
+//   sel[h][i]   = top-k video key tiles of video query tile i by S (and,
+//                 with a reference keep ratio -- the OmniRef page, "Device
+//                 profiles" -- its best reference (cond) tiles before them)
 //   c[h][i][:]  = softmax_j(S[h][i][j] / sqrt(D)) @ pooled v  (compression)
 //
 // Scores are evaluated in a fixed order -- start at +0, add the separately
@@ -15,11 +17,11 @@
 //                 staged transposed in LDS in chunks of 32 channels;
 //   softmax_topk  one wave per (head, query tile): the row lives in
 //                 registers; an MSB-first bitwise search finds the k-th
-//                 largest key, ties are admitted in ascending index order,
-//                 the kept indices are compacted in ascending order (with
-//                 their counts below each key-chunk boundary of the fine
-//                 branch); the row is then overwritten with its softmax
-//                 probabilities;
+//                 largest key of each group (video tiles; reference tiles),
+//                 ties are admitted in ascending index order, the kept
+//                 indices are compacted in ascending order (with their counts
+//                 below each key-chunk boundary of the fine branch); the row
+//                 is then overwritten with its softmax probabilities;
 //   pv            c = probabilities @ pooled v, 64 rows x D per block.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -101,13 +103,33 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Largest T with #{ok keys >= T} >= k (the k-th largest ok key), and how
+// many keys equal to T are still to be admitted.  Counts are ballots and
+// popcounts (scalar unit), not lane sums.  Every real key is nonzero (finite
+// scores map above 2^23), so candidates >= 1 never count a zero key.
 template <int MAXM>
-__global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(float* __restrict__ S, int H,
-                                                                  int Nt, int Ns, int P, int NV,
-                                                                  int topk, float scale_log2,
-                                                                  int32_t* __restrict__ sel,
-                                                                  int nchunks, int chunk_tiles,
-                                                                  int32_t* __restrict__ choff) {
+__device__ __forceinline__ void kth_key(const uint32_t (&key)[MAXM], const bool (&ok)[MAXM],
+                                        int k, uint32_t& thr, int& need) {
+  thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m)
+      c += __popcll(__builtin_amdgcn_ballot_w64(ok[m] && key[m] >= cand));
+    if (c >= k) thr = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) gt += __popcll(__builtin_amdgcn_ballot_w64(ok[m] && key[m] > thr));
+  need = k - gt;
+}
+
+template <int MAXM>
+__global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(
+    float* __restrict__ S, int H, int Nt, int Ns, int P, int NV, int topk, float scale_log2,
+    int32_t* __restrict__ sel, int nchunks, int chunk_tiles, int32_t* __restrict__ choff,
+    const int32_t* __restrict__ kind, int topk_ref, int32_t* __restrict__ visit, int visit_len) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= H * Nt) return;  // wave-uniform
@@ -123,54 +145,63 @@ __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(float* __restr
   }
 
   if (i >= P && topk > 0) {
-    // Keys of the video key tiles j in [P, Nt).
+    // Keys of every tile; the groups are the video key tiles j in [P, Nt)
+    // and, with a reference selection, the reference tiles among 0..P-1.
+    const bool refsel = topk_ref > 0;
     uint32_t key[MAXM];
-    bool ok[MAXM];
+    bool okv[MAXM], okr[MAXM], fixed[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
       const int j = lane + 64 * m;
-      ok[m] = j >= P && j < Nt;
-      key[m] = ok[m] ? order_key(s[m]) : 0u;
+      okv[m] = j >= P && j < Nt;
+      okr[m] = refsel && j < P && kind[j] == kKindRefTile;
+      fixed[m] = refsel && j < P && !okr[m];
+      key[m] = j < Nt ? order_key(s[m]) : 0u;
     }
-    // Largest T with #{key >= T} >= topk, i.e. the topk-th largest key.
-    // Counts are ballots and popcounts (scalar unit), not lane sums.  Slots
-    // that are not video key tiles hold key 0, which no candidate (>= 1)
-    // reaches; every real key is nonzero (finite scores map above 2^23).
-    uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int c = 0;
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m) c += __popcll(__builtin_amdgcn_ballot_w64(key[m] >= cand));
-      if (c >= topk) thr = cand;
-    }
-    int gt = 0;
-#pragma unroll
-    for (int m = 0; m < MAXM; ++m) gt += __popcll(__builtin_amdgcn_ballot_w64(key[m] > thr));
-    const int need = topk - gt;  // ties to admit, lowest index first
+    uint32_t thr_v, thr_r = 0;
+    int need_v, need_r = 0;  // ties to admit, lowest index first
+    kth_key<MAXM>(key, okv, topk, thr_v, need_v);
+    if (refsel) kth_key<MAXM>(key, okr, topk_ref, thr_r, need_r);
     const uint64_t below = (uint64_t(1) << lane) - 1;
-    // Lane c <= nchunks also counts the kept ids below c * chunk_tiles (the
-    // key-chunk boundaries of the fine branch): the count before block xm
-    // plus the kept lanes of block xm below xr.
+    // Lane c <= nchunks also counts the entries of the fine branch's list
+    // (visit with a reference selection, else sel) below c * chunk_tiles (the
+    // key-chunk boundaries): the count before block xm plus the listed
+    // lanes of block xm below xr.
     const int xb = min(lane * chunk_tiles, Nt);
     const int xm = xb >> 6, xr = xb & 63;
-    int below_x = topk;
-    int tie_base = 0, out_base = 0;
-    int32_t* dst = sel + (static_cast<size_t>(h) * NV + (i - P)) * topk;
+    int below_x = refsel ? visit_len : topk;
+    int tie_v = 0, tie_r = 0, out_s = 0, out_l = 0;
+    const size_t row = static_cast<size_t>(h) * NV + (i - P);
+    int32_t* dst = sel + row * (topk_ref + topk);
+    int32_t* vdst = refsel ? visit + row * visit_len : nullptr;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
-      const bool tie = ok[m] && key[m] == thr;
-      const uint64_t tmask = __ballot(tie);
-      const int rank = tie_base + __popcll(tmask & below);
-      tie_base += __popcll(tmask);
-      const bool take = ok[m] && (key[m] > thr || (tie && rank < need));
+      const bool tv = okv[m] && key[m] == thr_v;
+      const uint64_t tvmask = __ballot(tv);
+      const int rank_v = tie_v + __popcll(tvmask & below);
+      tie_v += __popcll(tvmask);
+      bool take = okv[m] && (key[m] > thr_v || (tv && rank_v < need_v));
+      if (refsel) {
+        const bool tr = okr[m] && key[m] == thr_r;
+        const uint64_t trmask = __ballot(tr);
+        const int rank_r = tie_r + __popcll(trmask & below);
+        tie_r += __popcll(trmask);
+        take = take || (okr[m] && (key[m] > thr_r || (tr && rank_r < need_r)));
+      }
       const uint64_t omask = __ballot(take);
-      if (take) dst[out_base + __popcll(omask & below)] = lane + 64 * m;
-      if (m == xm) below_x = out_base + __popcll(omask & ((uint64_t(1) << xr) - 1));
-      out_base += __popcll(omask);
+      if (take) dst[out_s + __popcll(omask & below)] = lane + 64 * m;
+      out_s += __popcll(omask);
+      uint64_t lmask = omask;
+      if (refsel) {
+        const bool listed = take || fixed[m];
+        lmask = __ballot(listed);
+        if (listed) vdst[out_l + __popcll(lmask & below)] = lane + 64 * m;
+      }
+      if (m == xm) below_x = out_l + __popcll(lmask & ((uint64_t(1) << xr) - 1));
+      out_l += __popcll(lmask);
     }
     if (nchunks > 1 && lane <= nchunks)
-      choff[(static_cast<size_t>(h) * NV + (i - P)) * (nchunks + 1) + lane] = below_x;
+      choff[row * (nchunks + 1) + lane] = below_x;
   }
 
   // Softmax over all key tiles with the 1/sqrt(D) scale (log2 domain).
@@ -290,7 +321,7 @@ hipError_t launch_d(const CoarseArgs& a, hipStream_t stream) {
 #define VSA_TOPK(M)                                                                           \
   hipLaunchKernelGGL((coarse_softmax_topk_kernel<M>), g2, dim3(256), 0, stream, a.scores, a.H, \
                      a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks,              \
-                     a.chunk_tiles, a.choff)
+                     a.chunk_tiles, a.choff, a.kind, a.topk_ref, a.visit, a.visit_len)
   if (maxm <= 4) VSA_TOPK(4);
   else if (maxm <= 8) VSA_TOPK(8);
   else if (maxm <= 12) VSA_TOPK(12);

@@ -5,19 +5,27 @@
 // Sparse Attention is not optional here"; FastH3 NVFP4 on RTX PRO 6000,
 // "Block-sparse FP4 attention for VSA tiles"): a video query tile attends to
 // every prefix key tile plus its selected video key tiles; a prefix query
-// tile attends to all tiles; pad keys of partial tiles are masked.  Then
+// tile attends to all tiles; pad keys of partial tiles are masked.  With a
+// reference keep ratio (the OmniRef page, "Device profiles") a video query
+// tile visits only its selected reference (cond) tiles among the prefix
+// tiles, and its whole key list comes from the coarse stage.  Then
 //     out[r] = o[r] + gate[r] * c[tile(r)]
 // written at the token's packed row ("Model integration": the output is
 // gathered back to packed order; the per-token gate multiplies the small
 // per-tile compression output, "What was tried and not shipped").
 //
 // Design (gfx950, wave64):
-//   - one block of 2 waves per (head, query tile); wave w owns query rows
-//     32w..32w+31 of the 64-row tile, gathered straight from the packed
-//     [L][H][D] input through the tile's slot table into MFMA operand
+//   - tiles hold 64 or 128 tokens and are handled as 64-slot blocks (a
+//     128-token tile is two consecutive blocks);
+//   - one block of 2 waves per (head, query block); wave w owns query rows
+//     32w..32w+31 of the 64-row block, gathered straight from the packed
+//     [L][H][D] input through the block's slot table into MFMA operand
 //     registers;
-//   - the visit list is ascending (prefix tiles 0..P-1, then the selected
-//     video tiles), so every row starts from a finite running max;
+//   - the visit list is ascending (prefix tiles 0..P-1, or the listed ones,
+//     then the selected video tiles) and visits each tile's blocks in order;
+//     a tile's first block always holds a token, so every row has a finite
+//     running max before a block without valid keys (the second block of a
+//     short 128-token tile) can come up;
 //   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
 //     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
 //     global->LDS loads (global_load_lds_dwordx4, no register staging).  A
@@ -108,10 +116,10 @@ struct IoOps<float> {  // fp32 I/O; the MFMA operands are rounded to bf16
   }
 };
 
-// (head, query tile) of block b in a single-launch forward.  With heads
-// divisible by 8, XCD x (blocks b = x mod 8) owns heads x, x+8, ...; inside
-// an XCD, the prefix items of its heads come first, then the video items
-// head by head.
+// (head, query item) of block b in a single-launch forward, for P prefix and
+// NV video items per head.  With heads divisible by 8, XCD x (blocks b = x
+// mod 8) owns heads x, x+8, ...; inside an XCD, the prefix items of its heads
+// come first, then the video items head by head.
 __device__ __forceinline__ void decode_item(int b, int H, int P, int NV, int& h, int& i) {
   if ((H & 7) == 0) {
     const int x = b & 7;
@@ -139,18 +147,19 @@ __device__ __forceinline__ void decode_item(int b, int H, int P, int NV, int& h,
   }
 }
 
-// (head, query tile) of block b in one key-chunk launch: XCD x works through
-// its heads x, x+8, ... one at a time, every query tile of a head in turn, so
-// the XCD's L2 only has to hold the current head's chunk of K and V.
-__device__ __forceinline__ void decode_item_chunked(int b, int H, int Nt, int& h, int& i) {
+// (head, query item) of block b in one key-chunk launch, for n items per
+// head: XCD x works through its heads x, x+8, ... one at a time, every query
+// item of a head in turn, so the XCD's L2 only has to hold the current head's
+// chunk of K and V.
+__device__ __forceinline__ void decode_item_chunked(int b, int H, int n, int& h, int& i) {
   if ((H & 7) == 0) {
     const int s = b >> 3;
-    const int k = s / Nt;
-    i = s - k * Nt;
+    const int k = s / n;
+    i = s - k * n;
     h = (b & 7) + 8 * k;
   } else {
-    h = b / Nt;
-    i = b - h * Nt;
+    h = b / n;
+    i = b - h * n;
   }
 }
 
@@ -182,7 +191,7 @@ __device__ __forceinline__ void load_f32x8(const TIO* p, float v[8]) {
 template <typename TIO, int D, bool QK8>
 __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
                                                           const int32_t* __restrict__ valid,
-                                                          const int32_t* __restrict__ sel,
+                                                          const int32_t* __restrict__ list,
                                                           const int32_t* __restrict__ choff,
                                                           float* __restrict__ state, int chunk) {
   // K rows: bf16 (2D bytes), or OCP FP8 E4M3 codes (D bytes) with QK8.
@@ -210,19 +219,25 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   const int lane = tid & 63;
   const int hl = lane >> 5;      // lane half: k-slots 8*hl..8*hl+7 of each MFMA
   const int l32 = lane & 31;
-  const int H = a.H, Nt = a.Nt, P = a.P, NV = a.NV, topk = a.topk;
+  const int H = a.H, Nt = a.Nt, P = a.P, NV = a.NV;
+  // Tiles are 1 << bsh blocks of 64 slots; the block is the unit of work.
+  const int bsh = a.bsh, Nb = Nt << bsh, Pvis = a.Pvis;
 
-  int hd, i;
+  int hd, ib;  // head, query block
   if (a.nchunks > 1)
-    decode_item_chunked(blockIdx.x, H, Nt, hd, i);
+    decode_item_chunked(blockIdx.x, H, Nb, hd, ib);
   else
-    decode_item(blockIdx.x, H, P, NV, hd, i);
+    decode_item(blockIdx.x, H, P << bsh, NV << bsh, hd, ib);
+  const int i = ib >> bsh;  // query tile
+  // The second block of a 128-token tile with at most 64 tokens has no rows.
+  if (valid[ib] == 0) return;
 
-  // Visit list: prefix tiles 0..P-1 then the selected video tiles (all
-  // tiles for a prefix query tile), ascending.  This launch covers the part
-  // of it with ids in [chunk * chunk_tiles, (chunk + 1) * chunk_tiles).
+  // Visit list of tiles: prefix tiles 0..Pvis-1 then the query tile's row of
+  // the list (all tiles for a prefix query tile), ascending; every tile is
+  // visited block by block.  This launch covers the part of it with ids in
+  // [chunk * chunk_tiles, (chunk + 1) * chunk_tiles).
   const bool dense = i < P;
-  int beg = 0, end = dense ? Nt : P + topk;
+  int beg = 0, end = dense ? Nt : Pvis + a.listlen;
   if (a.nchunks > 1) {
     const int lo = chunk * a.chunk_tiles;
     const int hi = min(lo + a.chunk_tiles, Nt);
@@ -231,10 +246,12 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
       end = hi;
     } else {
       const int32_t* co = choff + (static_cast<size_t>(hd) * NV + (i - P)) * (a.nchunks + 1) + chunk;
-      beg = min(lo, P) + co[0];
-      end = min(hi, P) + co[1];
+      beg = min(lo, Pvis) + co[0];
+      end = min(hi, Pvis) + co[1];
     }
   }
+  beg <<= bsh;
+  end <<= bsh;
   const bool first = chunk == 0;
   const bool last = chunk == a.nchunks - 1;
   // Nothing to add, and the running state stays where it is.
@@ -242,10 +259,10 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 
   // Query fragment: B operand of S^T = K Q^T (column = query, k = channel).
   const TIO* q = static_cast<const TIO*>(a.q);
-  const int pr = a.perm[static_cast<size_t>(i) * 64 + 32 * w + l32];
-  // A wave whose 32 query rows are all pad slots (the second half of a tile
+  const int pr = a.perm[static_cast<size_t>(ib) * 64 + 32 * w + l32];
+  // A wave whose 32 query rows are all pad slots (the second half of a block
   // with at most 32 valid tokens) only takes part in the loads and barriers.
-  const bool active = 32 * w < valid[i];
+  const bool active = 32 * w < valid[ib];
   // Rows come from the packed input, or from the tile-ordered copy that the
   // gather wrote after QK-norm and RoPE (pad rows are zero there).
   bf16x8 qf[QK8 ? 1 : NCK];
@@ -262,7 +279,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
       for (int g = 0; g < 4; ++g) {
         const int d0 = 64 * m + 32 * hl + 8 * g;
         if (a.qt) {
-          load_f32x8(a.qt + ((static_cast<size_t>(hd) * Nt + i) * 64 + 32 * w + l32) * D + d0,
+          load_f32x8(a.qt + ((static_cast<size_t>(hd) * Nb + ib) * 64 + 32 * w + l32) * D + d0,
                      &x[m][8 * g]);
         } else if (pr >= 0) {
           load_f32x8(q + (static_cast<size_t>(pr) * H + hd) * D + d0, &x[m][8 * g]);
@@ -290,7 +307,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
         qf8[m][j] = static_cast<int>(u);
       }
   } else if (a.qt) {
-    const uint16_t* qrow = a.qt + ((static_cast<size_t>(hd) * Nt + i) * 64 + 32 * w + l32) * D;
+    const uint16_t* qrow = a.qt + ((static_cast<size_t>(hd) * Nb + ib) * 64 + 32 * w + l32) * D;
 #pragma unroll
     for (int c = 0; c < NCK; ++c) qf[c] = IoOps<uint16_t>::load8(qrow + 16 * c + 8 * hl);
   } else {
@@ -303,17 +320,20 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
     }
   }
 
-  const int32_t* sl = sel + (dense ? 0 : (static_cast<size_t>(hd) * NV + (i - P)) * topk);
+  const int32_t* sl = list + (dense ? 0 : (static_cast<size_t>(hd) * NV + (i - P)) * a.listlen);
   const char* kth = (QK8 ? reinterpret_cast<const char*>(a.kt8) : reinterpret_cast<const char*>(a.kt)) +
-                    static_cast<size_t>(hd) * Nt * K_TILE;
+                    static_cast<size_t>(hd) * Nb * K_TILE;
   const char* ksh =
-      QK8 ? reinterpret_cast<const char*>(a.kscale) + static_cast<size_t>(hd) * Nt * 256 : nullptr;
-  const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nt * V_TILE;
-  // Listed ids are clamped into [0, Nt): a corrupt list can give a wrong
-  // result but never an out-of-bounds read.
+      QK8 ? reinterpret_cast<const char*>(a.kscale) + static_cast<size_t>(hd) * Nb * 256 : nullptr;
+  const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nb * V_TILE;
+  // Block of visit it.  Listed ids are clamped into [0, Nt): a corrupt list
+  // can give a wrong result but never an out-of-bounds read.
+  const int bmask = (1 << bsh) - 1;
   auto tile_at = [&](int it) -> int {
-    const int t = (dense || it < P) ? it : sl[it - P];
-    return min(max(t, 0), Nt - 1);
+    const int v = it >> bsh;
+    if (dense || v < Pvis) return it;
+    const int t = min(max(sl[v - Pvis], 0), Nt - 1);
+    return (t << bsh) | (it & bmask);
   };
 
   // LDS slot layouts (16-byte chunks, XOR-swizzled inside 64-byte rows so
@@ -391,7 +411,11 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 
   // Logit scale in log2 units; with QK8 it also carries the query row's
   // dequantisation scale (the key scales are applied to S below).
-  const float scale_log2 = (1.4426950408889634f / sqrtf(static_cast<float>(D))) * qsc;
+  // A query row of zeros has qsc 0 and all-zero logits; the scale then stays
+  // at its positive bf16 value so that masked keys (-inf) give exp2 = 0
+  // rather than -inf * 0.
+  const float scale_log2 = (1.4426950408889634f / sqrtf(static_cast<float>(D))) *
+                           (qsc > 0.0f ? qsc : 1.0f);
   // Running state of this wave's 32 rows: O^T accumulators, running max (in
   // log2 units) and this lane's partial row sum.  Between key-chunk launches
   // it lives in `state`, one 16-byte quad per lane per 4 words, coalesced:
@@ -400,7 +424,7 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x4* wstate = reinterpret_cast<f32x4*>(state) +
-                  ((static_cast<size_t>(hd) * Nt + i) * 2 + w) * (4 * NB + 1) * 64 + lane;
+                  ((static_cast<size_t>(hd) * Nb + ib) * 2 + w) * (4 * NB + 1) * 64 + lane;
   if (!first && active) {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
@@ -735,11 +759,11 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
 
 template <typename TIO, int D, bool QK8>
 hipError_t launch_q(const FineArgs& a, hipStream_t stream) {
-  const int blocks = a.H * a.Nt;
+  const int blocks = a.H * (a.Nt << a.bsh);
   const int nchunks = a.nchunks > 1 ? a.nchunks : 1;
   for (int c = 0; c < nchunks; ++c) {
     hipLaunchKernelGGL((fine_attn_kernel<TIO, D, QK8>), dim3(blocks), dim3(128), 0, stream, a,
-                       a.valid, a.sel, a.choff, a.state, c);
+                       a.valid, a.list, a.choff, a.state, c);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -11,52 +11,68 @@ struct QkPrepArgs {
   const float *q_weight, *k_weight;  // [D]
   const float *cos, *sin;            // [L][D/2], packed token order
   float eps;
-  uint16_t* qt;                      // [H][Nt][64][D] bf16: normalised, rotated q
+  uint16_t* qt;                      // [H][Nb][64][D] bf16: normalised, rotated q
 };
 
+// Nt counts tiles; a tile is 1 << bsh blocks of 64 slots (bsh 0: 64-token
+// tiles, 1: 128-token tiles), Nb = Nt << bsh blocks.
 struct PermutePoolArgs {
   const void *q, *k, *v;        // [L][H][D], bf16 or fp32
   bool io_f32;
-  const int32_t* perm;          // [Nt][64]
-  const int32_t* valid;         // [Nt]
-  int H, Nt, D;
-  uint16_t *kt, *vt;            // [H][Nt][64][D], [H][Nt][D][64] bf16
+  const int32_t* perm;          // [Nb][64]
+  const int32_t* valid;         // [Nb] valid slots per block
+  int H, Nt, D, bsh;
+  uint16_t *kt, *vt;            // [H][Nb][64][D], [H][Nb][2][D][32] bf16
   float *qp, *kp, *vp;          // [H][Nt][D]
   QkPrepArgs prep;
-  uint8_t* kt8;                 // [H][Nt][64][D] E4M3 keys instead of kt, or null
-  float* kscale;                // [H][Nt][64] per-key scale (with kt8)
+  uint8_t* kt8;                 // [H][Nb][64][D] E4M3 keys instead of kt, or null
+  float* kscale;                // [H][Nb][64] per-key scale (with kt8)
 };
 hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t stream);
 
+constexpr int32_t kKindRefTile = 1;
 struct CoarseArgs {
   const float *qp, *kp, *vp;    // [H][Nt][D]
   float* scores;                // [H][Nt][Ns]
   float* coarse;                // [H][Nt][D]
-  int32_t* sel;                 // [H][NV][topk]
+  int32_t* sel;                 // [H][NV][topk_ref + topk]: selected reference, then video tiles
   int32_t* choff;               // [H][NV][nchunks + 1], written if nchunks > 1
   int H, Nt, Ns, P, NV, topk, D;
   int nchunks, chunk_tiles;
+  // Reference selection (topk_ref > 0): kind [Nt] marks the reference tiles
+  // (value kKindRefTile);
+  // visit [H][NV][visit_len] receives every key tile a video query visits
+  // (fixed prefix, selected reference and video tiles, ascending), and choff
+  // then counts entries of visit instead of sel.
+  const int32_t* kind;
+  int topk_ref;
+  int32_t* visit;
+  int visit_len;
 };
 hipError_t launch_coarse(const CoarseArgs& a, hipStream_t stream);
 
+// Key tiles visited by a video query tile: tiles 0..Pvis-1, then its row of
+// `list` (listlen tile ids, ascending); a prefix query tile visits every tile.
 struct FineArgs {
   const void* q;                // [L][H][D] io dtype (unused if qt is set)
-  const uint16_t* qt;           // [H][Nt][64][D] bf16 tile-ordered q, or null
+  const uint16_t* qt;           // [H][Nb][64][D] bf16 tile-ordered q, or null
   const void* gate;             // [L][H][D] io dtype
   void* out;                    // [L][H][D] io dtype
   bool io_f32;
-  const uint16_t* kt;           // [H][Nt][64][D] bf16
-  const uint16_t* vt;           // [H][Nt][D][64] bf16
+  const uint16_t* kt;           // [H][Nb][64][D] bf16
+  const uint16_t* vt;           // [H][Nb][2][D][32] bf16
   const float* coarse;          // [H][Nt][D]
-  const int32_t* perm;          // [Nt][64]
-  const int32_t* valid;         // [Nt]
-  const int32_t* sel;           // [H][NV][topk]
-  const int32_t* choff;         // [H][NV][nchunks + 1] (nchunks > 1)
+  const int32_t* perm;          // [Nb][64]
+  const int32_t* valid;         // [Nb]
+  const int32_t* list;          // [H][NV][listlen]
+  const int32_t* choff;         // [H][NV][nchunks + 1] (nchunks > 1): list entries below
+                                // each chunk boundary
   float* state;                 // running softmax state between chunks (nchunks > 1)
-  int H, Nt, P, NV, topk, D;
+  int H, Nt, P, NV, listlen, D;
   int nchunks, chunk_tiles;
-  const uint8_t* kt8;           // [H][Nt][64][D] E4M3 keys: FP8 Q/K logits, or null
-  const float* kscale;          // [H][Nt][64]
+  const uint8_t* kt8;           // [H][Nb][64][D] E4M3 keys: FP8 Q/K logits, or null
+  const float* kscale;          // [H][Nb][64]
+  int bsh, Pvis;
 };
 hipError_t launch_fine(const FineArgs& a, hipStream_t stream);
 

@@ -5,8 +5,9 @@
 // Preview, "Video Sparse Attention is not optional here": tile scores come
 // from pooled q and k in fp32, and the compression branch uses pool(v).
 //
-// One block per (head, tile).  The tile's 64 slots of q, k and v are staged
-// in LDS (pad slots zero), then
+// One block per (head, tile).  A tile is one or two 64-slot blocks (64- or
+// 128-token tiles; block b holds slots 64b..64b+63).  For each block in turn
+// its 64 slots of q, k and v are staged in LDS (pad slots zero), then
 //   - k is written to Kt[h][tile][slot][d] (bf16),
 //   - v is written transposed to Vt[h][tile][half][d][pos] (bf16, positions
 //     0-31 and 32-63 in two halves, so that the fine kernel can fetch a half
@@ -14,9 +15,10 @@
 //     storage order is slots 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the slot
 //     swapped), so that the 8 keys one MFMA lane contracts over are adjacent;
 //   - q, k, v are mean-pooled per channel: a sequential fp32 sum over the
-//     valid slots in slot order, then one correctly rounded division by the
-//     count.  That fixed order makes the pooled values, and therefore the
-//     top-k selection, reproducible bit for bit.
+//     tile's valid slots in slot order (carried from block to block), then
+//     one correctly rounded division by the count.  That fixed order makes
+//     the pooled values, and therefore the top-k selection, reproducible bit
+//     for bit.
 // q itself is not permuted: the fine kernel gathers query rows directly.
 //
 // Optionally (PREP) q and k are first put through QK-norm and RoPE on the
@@ -47,7 +49,7 @@ __device__ __forceinline__ void store_pair(float* p, float a, float b) {
 template <typename T, int D, bool PREP>
 __global__ __launch_bounds__(384) void permute_pool_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ valid, int H, int Nt,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ valid, int H, int Nt, int bsh,
     uint16_t* __restrict__ kt, uint16_t* __restrict__ vt, float* __restrict__ qp,
     float* __restrict__ kp, float* __restrict__ vp, QkPrepArgs prep, uint8_t* __restrict__ kt8,
     float* __restrict__ kscale) {
@@ -60,198 +62,210 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
   __shared__ __attribute__((aligned(16))) T lds[3][64][D + kPad];
 
   const int h = blockIdx.x;
-  const int j = blockIdx.y;
+  const int tile = blockIdx.y;
   const int tid = threadIdx.x;
-  const int n = valid[j];
-  const int32_t* tperm = perm + static_cast<size_t>(j) * 64;
-
-  // Stage q, k, v rows of this tile (16-byte chunks, a whole row contiguous
-  // in memory): the slot table first, then every load of this thread before
-  // any LDS store, so that the loads are in flight together.
+  const int Nb = Nt << bsh;
   __shared__ int sperm[64];
-  if (tid < 64) sperm[tid] = tid < n ? tperm[tid] : -1;
-  __syncthreads();
-  static_assert((3 * kChunksPerTensor) % 384 == 0, "staging split");
-  constexpr int PER = 3 * kChunksPerTensor / 384;
-  uint4 val[PER];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int c = tid + 384 * r;
-    const int x = c / kChunksPerTensor;
-    const int rem = c - x * kChunksPerTensor;
-    const int slot = rem / kChunksPerRow;
-    const int part = rem - slot * kChunksPerRow;
-    const T* src = x == 0 ? q : (x == 1 ? k : v);
-    const int row = sperm[slot];
-    val[r] = make_uint4(0, 0, 0, 0);
-    if (row >= 0)
-      val[r] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) +
-                                               (static_cast<size_t>(row) * H + h) * kRowBytes +
-                                               part * 16);
-  }
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int c = tid + 384 * r;
-    const int x = c / kChunksPerTensor;
-    const int rem = c - x * kChunksPerTensor;
-    const int slot = rem / kChunksPerRow;
-    const int part = rem - slot * kChunksPerRow;
-    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&lds[x][slot][0]) + part * 16) = val[r];
-  }
-  __syncthreads();
+  // Pooling: one thread per (tensor, channel), fp32 sum over the tile's slots.
+  float pacc = 0.0f;
+  int ntile = 0;
 
-  if constexpr (PREP) {
-    __shared__ float rinv[2][64];
-    // Each thread's cos/sin entries for the rotation below, requested up
-    // front so that they arrive while the norms are computed (q and k of one
-    // (slot, pair) share them).
-    constexpr int PAIRS = D / 2;
-    constexpr int ITER = (64 * PAIRS + 383) / 384;
-    float cs[ITER], sn[ITER];
+  for (int blk = 0; blk < (1 << bsh); ++blk) {
+    const int j = (tile << bsh) + blk;   // block
+    const int n = valid[j];
+    ntile += n;
+    const int32_t* tperm = perm + static_cast<size_t>(j) * 64;
+
+    // Stage q, k, v rows of this block (16-byte chunks, a whole row contiguous
+    // in memory): the slot table first, then every load of this thread before
+    // any LDS store, so that the loads are in flight together.
+    if (tid < 64) sperm[tid] = tid < n ? tperm[tid] : -1;
+    __syncthreads();
+    static_assert((3 * kChunksPerTensor) % 384 == 0, "staging split");
+    constexpr int PER = 3 * kChunksPerTensor / 384;
+    uint4 val[PER];
 #pragma unroll
-    for (int r = 0; r < ITER; ++r) {
+    for (int r = 0; r < PER; ++r) {
       const int c = tid + 384 * r;
-      const int s = c / PAIRS;
-      cs[r] = 1.0f;
-      sn[r] = 0.0f;
-      if (c < 64 * PAIRS && s < n) {
-        const size_t t = static_cast<size_t>(sperm[s]) * PAIRS + (c - s * PAIRS);
-        cs[r] = prep.cos[t];
-        sn[r] = prep.sin[t];
-      }
+      const int x = c / kChunksPerTensor;
+      const int rem = c - x * kChunksPerTensor;
+      const int slot = rem / kChunksPerRow;
+      const int part = rem - slot * kChunksPerRow;
+      const T* src = x == 0 ? q : (x == 1 ? k : v);
+      const int row = sperm[slot];
+      val[r] = make_uint4(0, 0, 0, 0);
+      if (row >= 0)
+        val[r] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) +
+                                                 (static_cast<size_t>(row) * H + h) * kRowBytes +
+                                                 part * 16);
     }
-    // Inverse RMS of every valid q and k row, one thread per row.
-    if (tid < 128) {
-      const int x = tid >> 6, s = tid & 63;
-      float inv = 0.0f;
-      if (s < n) {
-#pragma clang fp contract(off)
-        float ss = 0.0f;
-        for (int d = 0; d < D; ++d) {
-          const float e = to_f32(lds[x][s][d]);
-          ss = ss + e * e;
-        }
-        const float ms = __fdiv_rn(ss, static_cast<float>(D));
-        inv = __fdiv_rn(1.0f, __builtin_sqrtf(ms + prep.eps));   // IEEE (correctly rounded)
-      }
-      rinv[x][s] = inv;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int c = tid + 384 * r;
+      const int x = c / kChunksPerTensor;
+      const int rem = c - x * kChunksPerTensor;
+      const int slot = rem / kChunksPerRow;
+      const int part = rem - slot * kChunksPerRow;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&lds[x][slot][0]) + part * 16) = val[r];
     }
     __syncthreads();
-    // Scale, weight and rotate every interleaved pair of the valid rows.
+
+    if constexpr (PREP) {
+      __shared__ float rinv[2][64];
+      // Each thread's cos/sin entries for the rotation below, requested up
+      // front so that they arrive while the norms are computed (q and k of one
+      // (slot, pair) share them).
+      constexpr int PAIRS = D / 2;
+      constexpr int ITER = (64 * PAIRS + 383) / 384;
+      float cs[ITER], sn[ITER];
 #pragma unroll
-    for (int r = 0; r < ITER; ++r) {
-      const int c = tid + 384 * r;
-      const int s = c / PAIRS;
-      const int i = c - s * PAIRS;
-      if (c < 64 * PAIRS && s < n) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-#pragma clang fp contract(off)
-          const float inv = rinv[x][s];
-          const float* w = x == 0 ? prep.q_weight : prep.k_weight;
-          const float a = (to_f32(lds[x][s][2 * i]) * inv) * w[2 * i];
-          const float b = (to_f32(lds[x][s][2 * i + 1]) * inv) * w[2 * i + 1];
-          store_pair(&lds[x][s][2 * i], a * cs[r] - b * sn[r], a * sn[r] + b * cs[r]);
+      for (int r = 0; r < ITER; ++r) {
+        const int c = tid + 384 * r;
+        const int s = c / PAIRS;
+        cs[r] = 1.0f;
+        sn[r] = 0.0f;
+        if (c < 64 * PAIRS && s < n) {
+          const size_t t = static_cast<size_t>(sperm[s]) * PAIRS + (c - s * PAIRS);
+          cs[r] = prep.cos[t];
+          sn[r] = prep.sin[t];
         }
       }
+      // Inverse RMS of every valid q and k row, one thread per row.
+      if (tid < 128) {
+        const int x = tid >> 6, s = tid & 63;
+        float inv = 0.0f;
+        if (s < n) {
+#pragma clang fp contract(off)
+          float ss = 0.0f;
+          for (int d = 0; d < D; ++d) {
+            const float e = to_f32(lds[x][s][d]);
+            ss = ss + e * e;
+          }
+          const float ms = __fdiv_rn(ss, static_cast<float>(D));
+          inv = __fdiv_rn(1.0f, __builtin_sqrtf(ms + prep.eps));   // IEEE (correctly rounded)
+        }
+        rinv[x][s] = inv;
+      }
+      __syncthreads();
+      // Scale, weight and rotate every interleaved pair of the valid rows.
+#pragma unroll
+      for (int r = 0; r < ITER; ++r) {
+        const int c = tid + 384 * r;
+        const int s = c / PAIRS;
+        const int i = c - s * PAIRS;
+        if (c < 64 * PAIRS && s < n) {
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+#pragma clang fp contract(off)
+            const float inv = rinv[x][s];
+            const float* w = x == 0 ? prep.q_weight : prep.k_weight;
+            const float a = (to_f32(lds[x][s][2 * i]) * inv) * w[2 * i];
+            const float b = (to_f32(lds[x][s][2 * i + 1]) * inv) * w[2 * i + 1];
+            store_pair(&lds[x][s][2 * i], a * cs[r] - b * sn[r], a * sn[r] + b * cs[r]);
+          }
+        }
+      }
+      __syncthreads();
     }
+
+    const size_t tile_base = static_cast<size_t>(h) * Nb + j;   // block row of Kt, Vt, ...
+
+    // Pool: continue the sequential fp32 sum in slot order.
+    if (tid < 3 * D) {
+#pragma clang fp contract(off)
+      const int x = tid / D;
+      const int d = tid - x * D;
+      for (int s = 0; s < n; ++s) pacc = pacc + to_f32(lds[x][s][d]);
+    }
+
+    // Keys as per-token FP8 (OCP E4M3) codes instead of bf16: amax of each
+    // valid row, codes of x * (448 / amax) (the division correctly rounded, the
+    // product rounded to fp32, the conversion to nearest even), and the
+    // dequantisation scale amax / 448; pad rows get zero codes and scale.
+    if (kt8) {
+      __shared__ float kinv[64];
+      if (tid < 64) {
+        float amax = 0.0f;
+        if (tid < n)
+          for (int d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(to_f32(lds[1][tid][d])));
+        kinv[tid] = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
+        kscale[tile_base * 64 + tid] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 0.0f;
+      }
+      __syncthreads();
+      uint8_t* dst = kt8 + tile_base * 64 * D;
+      for (int c = tid; c < 64 * (D / 16); c += blockDim.x) {
+        const int slot = c / (D / 16);
+        const int d0 = (c - slot * (D / 16)) * 16;
+        const float inv = kinv[slot];
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const T* e = &lds[1][slot][d0 + 4 * j];
+          uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(to_f32(e[0]) * inv, to_f32(e[1]) * inv, 0,
+                                                       false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(to_f32(e[2]) * inv, to_f32(e[3]) * inv, w, true);
+          o[j] = w;
+        }
+        *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
+      }
+    }
+
+    // Kt (and Qt with PREP): [slot][d] bf16, 16-byte chunks of 8 channels.
+    for (int x = PREP ? 0 : 1; x < (kt8 ? 1 : 2); ++x) {
+      uint16_t* dst = (x == 0 ? prep.qt : kt) + tile_base * 64 * D;
+      for (int c = tid; c < 64 * (D / 8); c += blockDim.x) {
+        const int slot = c / (D / 8);
+        const int d0 = (c - slot * (D / 8)) * 8;
+        uint4 o;
+        o.x = pack_bf16x2(to_f32(lds[x][slot][d0 + 0]), to_f32(lds[x][slot][d0 + 1]));
+        o.y = pack_bf16x2(to_f32(lds[x][slot][d0 + 2]), to_f32(lds[x][slot][d0 + 3]));
+        o.z = pack_bf16x2(to_f32(lds[x][slot][d0 + 4]), to_f32(lds[x][slot][d0 + 5]));
+        o.w = pack_bf16x2(to_f32(lds[x][slot][d0 + 6]), to_f32(lds[x][slot][d0 + 7]));
+        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
+      }
+    }
+    // Vt: two halves of positions (0-31, 32-63), each [d][32] bf16 with
+    // 16-byte chunks of 8 positions.  Positions p0..p0+7 (p0 = 8m) hold slots
+    // 16(m/2) + 4(m%2) + {0..3} and the same + 8.
+    {
+      uint16_t* dst = vt + tile_base * 64 * D;
+      for (int c = tid; c < D * 8; c += blockDim.x) {
+        const int d = c % D;
+        const int m = c / D;
+        const int sa = 16 * (m >> 1) + 4 * (m & 1);
+        const int sb = sa + 8;
+        uint4 o;
+        o.x = pack_bf16x2(to_f32(lds[2][sa + 0][d]), to_f32(lds[2][sa + 1][d]));
+        o.y = pack_bf16x2(to_f32(lds[2][sa + 2][d]), to_f32(lds[2][sa + 3][d]));
+        o.z = pack_bf16x2(to_f32(lds[2][sb + 0][d]), to_f32(lds[2][sb + 1][d]));
+        o.w = pack_bf16x2(to_f32(lds[2][sb + 2][d]), to_f32(lds[2][sb + 3][d]));
+        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(m >> 2) * 32 * D + d * 32 + 8 * (m & 3)) = o;
+      }
+    }
+    // Every read of this block's LDS rows is done before the next block's staging.
     __syncthreads();
   }
 
-  const size_t tile_base = static_cast<size_t>(h) * Nt + j;
-
-  // Pool: one thread per (tensor, channel), sequential fp32 sum in slot order.
   if (tid < 3 * D) {
     const int x = tid / D;
     const int d = tid - x * D;
-    float acc = 0.0f;
-    {
-#pragma clang fp contract(off)
-      for (int s = 0; s < n; ++s) acc = acc + to_f32(lds[x][s][d]);
-    }
-    const float mean = __fdiv_rn(acc, static_cast<float>(n));
     float* dst = x == 0 ? qp : (x == 1 ? kp : vp);
-    dst[tile_base * D + d] = mean;
-  }
-
-  // Keys as per-token FP8 (OCP E4M3) codes instead of bf16: amax of each
-  // valid row, codes of x * (448 / amax) (the division correctly rounded, the
-  // product rounded to fp32, the conversion to nearest even), and the
-  // dequantisation scale amax / 448; pad rows get zero codes and scale.
-  if (kt8) {
-    __shared__ float kinv[64];
-    if (tid < 64) {
-      float amax = 0.0f;
-      if (tid < n)
-        for (int d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(to_f32(lds[1][tid][d])));
-      kinv[tid] = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
-      kscale[tile_base * 64 + tid] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 0.0f;
-    }
-    __syncthreads();
-    uint8_t* dst = kt8 + tile_base * 64 * D;
-    for (int c = tid; c < 64 * (D / 16); c += blockDim.x) {
-      const int slot = c / (D / 16);
-      const int d0 = (c - slot * (D / 16)) * 16;
-      const float inv = kinv[slot];
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const T* e = &lds[1][slot][d0 + 4 * j];
-        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(to_f32(e[0]) * inv, to_f32(e[1]) * inv, 0,
-                                                     false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(to_f32(e[2]) * inv, to_f32(e[3]) * inv, w, true);
-        o[j] = w;
-      }
-      *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
-    }
-  }
-
-  // Kt (and Qt with PREP): [slot][d] bf16, 16-byte chunks of 8 channels.
-  for (int x = PREP ? 0 : 1; x < (kt8 ? 1 : 2); ++x) {
-    uint16_t* dst = (x == 0 ? prep.qt : kt) + tile_base * 64 * D;
-    for (int c = tid; c < 64 * (D / 8); c += blockDim.x) {
-      const int slot = c / (D / 8);
-      const int d0 = (c - slot * (D / 8)) * 8;
-      uint4 o;
-      o.x = pack_bf16x2(to_f32(lds[x][slot][d0 + 0]), to_f32(lds[x][slot][d0 + 1]));
-      o.y = pack_bf16x2(to_f32(lds[x][slot][d0 + 2]), to_f32(lds[x][slot][d0 + 3]));
-      o.z = pack_bf16x2(to_f32(lds[x][slot][d0 + 4]), to_f32(lds[x][slot][d0 + 5]));
-      o.w = pack_bf16x2(to_f32(lds[x][slot][d0 + 6]), to_f32(lds[x][slot][d0 + 7]));
-      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
-    }
-  }
-  // Vt: two halves of positions (0-31, 32-63), each [d][32] bf16 with
-  // 16-byte chunks of 8 positions.  Positions p0..p0+7 (p0 = 8m) hold slots
-  // 16(m/2) + 4(m%2) + {0..3} and the same + 8.
-  {
-    uint16_t* dst = vt + tile_base * 64 * D;
-    for (int c = tid; c < D * 8; c += blockDim.x) {
-      const int d = c % D;
-      const int m = c / D;
-      const int sa = 16 * (m >> 1) + 4 * (m & 1);
-      const int sb = sa + 8;
-      uint4 o;
-      o.x = pack_bf16x2(to_f32(lds[2][sa + 0][d]), to_f32(lds[2][sa + 1][d]));
-      o.y = pack_bf16x2(to_f32(lds[2][sa + 2][d]), to_f32(lds[2][sa + 3][d]));
-      o.z = pack_bf16x2(to_f32(lds[2][sb + 0][d]), to_f32(lds[2][sb + 1][d]));
-      o.w = pack_bf16x2(to_f32(lds[2][sb + 2][d]), to_f32(lds[2][sb + 3][d]));
-      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(m >> 2) * 32 * D + d * 32 + 8 * (m & 3)) = o;
-    }
+    dst[(static_cast<size_t>(h) * Nt + tile) * D + d] = __fdiv_rn(pacc, static_cast<float>(ntile));
   }
 }
 
 template <typename T, int D>
 hipError_t launch(const PermutePoolArgs& a, hipStream_t stream) {
-  dim3 grid(a.H, a.Nt);
+  dim3 grid(a.H, a.Nt);   // one block per (head, tile)
   if (a.prep.qt)
     hipLaunchKernelGGL((permute_pool_kernel<T, D, true>), grid, dim3(384), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.kt, a.vt,
+                       static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.bsh, a.kt, a.vt,
                        a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale);
   else
     hipLaunchKernelGGL((permute_pool_kernel<T, D, false>), grid, dim3(384), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.kt, a.vt,
+                       static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.bsh, a.kt, a.vt,
                        a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale);
   return hipGetLastError();
 }

@@ -2,6 +2,12 @@
 // "Video Sparse Attention is not optional here"): segment-pure prefix tiles
 // and (4,4,4) video tiles over the post-patchify grid, derived from the
 // packed stream's tags and positions; the top-k rule of the same passage.
+// The OmniRef page ("Device profiles") also runs 128-token tiles with a
+// reference keep ratio: here a video tile is any box of 64 or 128 grid cells,
+// prefix tiles hold as many tokens, and with keep r < 1 a video query tile
+// keeps only max(1, min(ceil(r * n_ref), n_ref)) of the n_ref cond tiles.
+// Kernels work on 64-token blocks: a 128-token tile is blocks 2j (slots
+// 0-63) and 2j + 1 (slots 64-127).
 #include "plan.hpp"
 
 #include <algorithm>
@@ -20,6 +26,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 void set_error(const std::string& msg) { g_error = msg; }
 const char* get_error() { return g_error.c_str(); }
 
+int64_t ref_keep_rule(int64_t n, double r) {
+  if (n <= 0) return 0;
+  double want = std::ceil(r * static_cast<double>(n));
+  int64_t k = want >= static_cast<double>(n) ? n : static_cast<int64_t>(want);
+  return k < 1 ? 1 : k;
+}
+
 int64_t topk_rule(int64_t nv, double s) {
   if (!(s >= 0.0 && s <= 1.0)) return -1;  // also rejects NaN
   if (nv <= 0) return 0;
@@ -36,6 +49,7 @@ void lay_out(vsa_h3_plan* plan) {
   const uint64_t h64 = static_cast<uint64_t>(plan->heads);
   const uint64_t d64 = static_cast<uint64_t>(plan->head_dim);
   const uint64_t nt64 = static_cast<uint64_t>(plan->Nt);
+  const uint64_t nb64 = static_cast<uint64_t>(plan->Nb);
   const uint64_t nv64 = static_cast<uint64_t>(plan->NV);
   const int64_t ns = (plan->Nt + 3) / 4 * 4;
   Layout& lo = plan->layout;
@@ -45,25 +59,27 @@ void lay_out(vsa_h3_plan* plan) {
     off = align256(off + bytes);
     return at;
   };
-  lo.perm = take(nt64 * kTile * 4);
-  lo.valid = take(nt64 * 4);
-  lo.kt = take(h64 * nt64 * kTile * d64 * 2);
-  lo.vt = take(h64 * nt64 * kTile * d64 * 2);
+  lo.perm = take(nb64 * kTile * 4);
+  lo.valid = take(nb64 * 4);
+  lo.kind = take(nt64 * 4);
+  lo.kt = take(h64 * nb64 * kTile * d64 * 2);
+  lo.vt = take(h64 * nb64 * kTile * d64 * 2);
   lo.qp = take(h64 * nt64 * d64 * 4);
   lo.kp = take(h64 * nt64 * d64 * 4);
   lo.vp = take(h64 * nt64 * d64 * 4);
   lo.scores = take(h64 * nt64 * static_cast<uint64_t>(ns) * 4);
   lo.coarse = take(h64 * nt64 * d64 * 4);
-  lo.sel = take(h64 * nv64 * static_cast<uint64_t>(plan->topk) * 4);
+  lo.sel = take(h64 * nv64 * static_cast<uint64_t>(sel_width(plan)) * 4);
+  lo.visit = take(plan->topk_ref > 0 ? h64 * nv64 * static_cast<uint64_t>(visit_len(plan)) * 4 : 0);
   const bool chunked = plan->num_chunks > 1;
   lo.choff = take(chunked ? h64 * nv64 * static_cast<uint64_t>(plan->num_chunks + 1) * 4 : 0);
-  // Two waves of 64 lanes per query tile.
-  lo.state = take(chunked ? h64 * nt64 * 2 * 64 *
+  // Two waves of 64 lanes per query block.
+  lo.state = take(chunked ? h64 * nb64 * 2 * 64 *
                                 static_cast<uint64_t>(state_words_per_lane(plan->head_dim)) * 4
                           : 0);
-  lo.qt = take(plan->qk_prep ? h64 * nt64 * kTile * d64 * 2 : 0);
-  lo.kt8 = take(plan->qk_fp8 ? h64 * nt64 * kTile * d64 : 0);
-  lo.kscale = take(plan->qk_fp8 ? h64 * nt64 * kTile * 4 : 0);
+  lo.qt = take(plan->qk_prep ? h64 * nb64 * kTile * d64 * 2 : 0);
+  lo.kt8 = take(plan->qk_fp8 ? h64 * nb64 * kTile * d64 : 0);
+  lo.kscale = take(plan->qk_fp8 ? h64 * nb64 * kTile * 4 : 0);
   lo.total = off < 256 ? 256 : off;
   lo.ns = ns;
 }
@@ -78,9 +94,10 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
   const int64_t Nt = plan->Nt;
   int64_t ch;
   if (chunk_tiles == 0) {
-    // Largest chunk within kChunkBytes of K and V (64 keys x D: K in bf16,
-    // or FP8 codes, plus bf16 V^T), then balanced over the chunks.
-    const uint64_t tile_bytes = uint64_t(64) * plan->head_dim * (plan->qk_fp8 ? 3 : 4);
+    // Largest chunk within kChunkBytes of K and V (tile_tokens keys x D: K
+    // in bf16, or FP8 codes, plus bf16 V^T), then balanced over the chunks.
+    const uint64_t tile_bytes =
+        uint64_t(plan->tile_tokens) * plan->head_dim * (plan->qk_fp8 ? 3 : 4);
     const int64_t cap = static_cast<int64_t>(kChunkBytes / tile_bytes);
     const int64_t nc = std::max<int64_t>(1, ceil_div(Nt, cap));
     ch = std::max<int64_t>(1, ceil_div(Nt, nc));
@@ -111,6 +128,17 @@ void set_qk_fp8(vsa_h3_plan* plan, bool enable) {
   if (plan->chunk_request != 0 || set_chunk_tiles(plan, 0) != VSA_OK) lay_out(plan);
 }
 
+vsa_status set_ref_keep(vsa_h3_plan* plan, double keep) {
+  if (!(keep > 0.0 && keep <= 1.0)) {  // also rejects NaN
+    set_error("the reference keep ratio must lie in (0, 1]");
+    return VSA_E_ARG;
+  }
+  plan->ref_keep = keep;
+  plan->topk_ref = keep < 1.0 ? ref_keep_rule(plan->num_ref, keep) : 0;
+  lay_out(plan);
+  return VSA_OK;
+}
+
 vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_dims3 grid,
                       vsa_dims3 tile, int32_t heads, int32_t head_dim, double sparsity,
                       vsa_h3_plan* plan) {
@@ -134,10 +162,13 @@ vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_di
     set_error("grid dimensions must be >= 0");
     return VSA_E_ARG;
   }
-  if (tile.t != 4 || tile.h != 4 || tile.w != 4) {
-    set_error("only (4,4,4) video tiles are implemented");
+  if (tile.t < 1 || tile.h < 1 || tile.w < 1 ||
+      (int64_t(tile.t) * tile.h * tile.w != 64 && int64_t(tile.t) * tile.h * tile.w != 128)) {
+    set_error("a video tile must be a box of 64 or 128 grid cells");
     return VSA_E_UNSUPPORTED;
   }
+  const int64_t tt = tile.t, th = tile.h, tw = tile.w;
+  const int64_t ntok = tt * th * tw;
   if (head_dim != 64 && head_dim != 128) {
     set_error("head_dim must be 64 or 128");
     return VSA_E_UNSUPPORTED;
@@ -168,22 +199,23 @@ vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_di
     return VSA_E_POSITIONS;
   }
 
-  // Prefix tiles: each maximal run of one tag is cut into 64-token chunks.
-  std::vector<int64_t> pre_start, pre_len;
+  // Prefix tiles: each maximal run of one tag is cut into tile-sized chunks.
+  std::vector<int64_t> pre_start, pre_len, pre_tag;
   for (int64_t s = 0; s < n_pre;) {
     int64_t e = s;
     while (e < n_pre && tags[e] == tags[s]) ++e;
-    for (int64_t c = s; c < e; c += kTile) {
+    for (int64_t c = s; c < e; c += ntok) {
       pre_start.push_back(c);
-      pre_len.push_back(std::min<int64_t>(kTile, e - c));
+      pre_len.push_back(std::min<int64_t>(ntok, e - c));
+      pre_tag.push_back(tags[s]);
     }
     s = e;
   }
   const int64_t P = static_cast<int64_t>(pre_start.size());
-  const int64_t nt = ceil_div(T, 4), nh = ceil_div(H, 4), nw = ceil_div(W, 4);
+  const int64_t nt = ceil_div(T, tt), nh = ceil_div(H, th), nw = ceil_div(W, tw);
   const int64_t NV = n_vid ? nt * nh * nw : 0;
   const int64_t Nt = P + NV;
-  if (Nt * kTile >= (int64_t(1) << 31)) {
+  if (Nt * ntok >= (int64_t(1) << 31)) {
     set_error("too many tiles for 32-bit slot indices");
     return VSA_E_UNSUPPORTED;
   }
@@ -200,20 +232,32 @@ vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_di
   plan->heads = heads;
   plan->head_dim = head_dim;
   plan->grid = grid;
+  plan->tile = tile;
+  plan->tile_tokens = static_cast<int32_t>(ntok);
+  plan->bsh = ntok == 128 ? 1 : 0;
+  plan->Nb = Nt << plan->bsh;
   plan->sparsity = sparsity;
-  plan->perm.assign(static_cast<size_t>(Nt * kTile), -1);
+  plan->perm.assign(static_cast<size_t>(Nt * ntok), -1);
   plan->valid.assign(static_cast<size_t>(Nt), 0);
+  plan->kind.assign(static_cast<size_t>(Nt), vsa::kKindVideo);
   plan->tile_slot.assign(static_cast<size_t>(L), -1);
+  plan->num_ref = 0;
+  for (int64_t j = 0; j < P; ++j) {
+    const bool ref = pre_tag[j] == VSA_TAG_COND;
+    plan->kind[j] = ref ? vsa::kKindRef : vsa::kKindPrefix;
+    plan->num_ref += ref;
+  }
+  plan->num_fixed = P - plan->num_ref;
 
   for (int64_t j = 0; j < P; ++j) {
     plan->valid[j] = static_cast<int32_t>(pre_len[j]);
     for (int64_t s = 0; s < pre_len[j]; ++s) {
-      plan->perm[j * kTile + s] = static_cast<int32_t>(pre_start[j] + s);
-      plan->tile_slot[pre_start[j] + s] = static_cast<int32_t>(j * kTile + s);
+      plan->perm[j * ntok + s] = static_cast<int32_t>(pre_start[j] + s);
+      plan->tile_slot[pre_start[j] + s] = static_cast<int32_t>(j * ntok + s);
     }
   }
 
-  // Video tiles: tile id from the (t/4, y/4, x/4) raster; the slot is the
+  // Video tiles: tile id from the (t/tt, y/th, x/tw) raster; the slot is the
   // compact (t, y, x) raster inside the tile's valid extent.
   std::vector<uint8_t> seen(static_cast<size_t>(n_vid), 0);
   for (int64_t r = n_pre; r < L; ++r) {
@@ -228,19 +272,27 @@ vsa_status build_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_di
       return VSA_E_POSITIONS;
     }
     seen[cell] = 1;
-    const int64_t bt = t / 4, by = y / 4, bx = x / 4;
-    const int64_t et = std::min<int64_t>(4, T - 4 * bt);
-    const int64_t eh = std::min<int64_t>(4, H - 4 * by);
-    const int64_t ew = std::min<int64_t>(4, W - 4 * bx);
+    const int64_t bt = t / tt, by = y / th, bx = x / tw;
+    const int64_t et = std::min<int64_t>(tt, T - tt * bt);
+    const int64_t eh = std::min<int64_t>(th, H - th * by);
+    const int64_t ew = std::min<int64_t>(tw, W - tw * bx);
     const int64_t j = P + (bt * nh + by) * nw + bx;
-    const int64_t slot = ((t % 4) * eh + (y % 4)) * ew + (x % 4);
+    const int64_t slot = ((t % tt) * eh + (y % th)) * ew + (x % tw);
     plan->valid[j] = static_cast<int32_t>(et * eh * ew);
-    plan->perm[j * kTile + slot] = static_cast<int32_t>(r);
-    plan->tile_slot[r] = static_cast<int32_t>(j * kTile + slot);
+    plan->perm[j * ntok + slot] = static_cast<int32_t>(r);
+    plan->tile_slot[r] = static_cast<int32_t>(j * ntok + slot);
   }
 
+  // Valid tokens of each 64-token block (slots fill a tile from the front).
+  plan->bvalid.assign(static_cast<size_t>(plan->Nb), 0);
+  for (int64_t j = 0; j < Nt; ++j)
+    for (int64_t b = 0; b < (int64_t(1) << plan->bsh); ++b)
+      plan->bvalid[(j << plan->bsh) + b] = static_cast<int32_t>(
+          std::max<int64_t>(0, std::min<int64_t>(kTile, plan->valid[j] - kTile * b)));
+
+  plan->ref_keep = 1.0;
+  plan->topk_ref = 0;
   return set_chunk_tiles(plan, 0);
-  return VSA_OK;
 }
 
 }  // namespace vsa

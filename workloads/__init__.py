@@ -45,6 +45,8 @@ class Workload:
     sparsity: float
     smooth: bool = False
     description: str = ""
+    tile: tuple = (4, 4, 4)        # video tile box (64 or 128 grid cells)
+    ref_keep: float = 1.0          # reference keep ratio (1: every cond tile visited)
 
     @property
     def n_prefix_tokens(self) -> int:
@@ -85,6 +87,24 @@ WORKLOADS = {
         (27, 48, 84), 0.9, smooth=True,
         description="768p 15-s shape: 111,936 tokens (3,072 prefix + 27x48x84 video; last "
                     "temporal tile row 3 frames), smooth+noise q/k, sparsity 0.9"),
+    # The OmniRef profile: VSA at sparsity 0.9 with 128-token tiles and
+    # reference keep 0.1 (the OmniRef page, "Device profiles").  Its reference
+    # prefix here is 4 images of 896x896 at one vision token per 28x28 pixels
+    # (4 x 1,024 cond tokens); the pages give no token counts for it.
+    "omniref768p10s": Workload(
+        "omniref768p10s", 56, 128, "bf16", ((TEXT, 512), (COND, 4096), (AUDIO, 512)),
+        (18, 48, 84), 0.9, tile=(4, 8, 4), ref_keep=0.1,
+        description="OmniRef 768p 10-s shape: 77,696 tokens (512 text + 4,096 reference + "
+                    "512 audio + 18x48x84 video), 56 heads, head_dim 128, bf16, sparsity 0.9, "
+                    "(4,8,4) 128-token tiles (the last temporal tile row holds 2 frames: "
+                    "64 tokens), reference keep 0.1"),
+    "omniref_small": Workload(
+        "omniref_small", 2, 128, "bf16", ((TEXT, 100), (COND, 700), (AUDIO, 60), (COND, 200)),
+        (10, 16, 12), 0.7, tile=(4, 8, 4), ref_keep=0.3,
+        description="small OmniRef layout: 2,980 tokens (1,060 prefix tokens in 10 tiles, 8 "
+                    "of them reference tiles, + 10x16x12 video in 18 tiles, those of the last "
+                    "temporal row 64 tokens each), 2 heads, head_dim 128, bf16, sparsity 0.7, "
+                    "reference keep 0.3"),
 }
 
 
