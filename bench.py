@@ -78,34 +78,66 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def fine_flops(sel: np.ndarray, valid: np.ndarray, P: int, L: int, D: int) -> tuple[float, float]:
-    """Algorithmic fine-branch FLOPs (valid tokens only) and the padded-tile
-    FLOPs the MFMA executes, for one forward.  sel: [H, NV, topk] global ids."""
-    H, NV, topk = sel.shape
+def _blocks(valid: np.ndarray, tile_tokens: int) -> np.ndarray:
+    """Valid tokens of each 64-slot block of every tile: [Nt, tile_tokens / 64]."""
+    b = np.arange(tile_tokens // 64)
+    return np.clip(valid.astype(np.int64)[:, None] - 64 * b[None, :], 0, 64)
+
+
+def fine_flops(sel: np.ndarray, valid: np.ndarray, P: int, L: int, D: int, fixed=None,
+               tile_tokens: int = 64) -> tuple[float, float]:
+    """Algorithmic fine-branch FLOPs (valid tokens only) and the padded-block
+    FLOPs the MFMA executes, for one forward.  sel: [H, NV, n] selected key
+    tiles (global ids) of each video query tile; fixed: the prefix tiles every
+    video query tile visits besides them (default: all P prefix tiles).  The
+    kernel works on 64-slot blocks: each query block that holds a token visits
+    every block of each listed key tile."""
+    H, NV, nsel = sel.shape
+    fixed = np.arange(P) if fixed is None else np.asarray(fixed, np.int64)
     n = valid.astype(np.float64)
-    p_tok = float(n[:P].sum())
-    per_row = p_tok + n[sel].sum(axis=2)                      # [H, NV] keys per video query
+    Nt = n.shape[0]
+    per_row = float(n[fixed].sum()) + n[sel].sum(axis=2)      # [H, NV] keys per video query
     video = float((per_row * n[P:][None, :]).sum())
     prefix = float(n[:P].sum()) * L * H
     alg = 4.0 * D * (video + prefix)
-    pairs = H * (NV * (P + topk) + P * (P + NV))
+    qb = (_blocks(valid, tile_tokens) > 0).sum(axis=1)          # query blocks with a token
+    kb = tile_tokens // 64
+    pairs = H * (float(qb[P:].sum()) * (len(fixed) + nsel) + float(qb[:P].sum()) * Nt) * kb
     padded = 4.0 * D * 64 * 64 * pairs
     return alg, padded
 
 
-def kv_stream_bytes(sel: np.ndarray, valid: np.ndarray, P: int, D: int, qk_fp8: bool) -> float:
+def kv_stream_bytes(sel: np.ndarray, valid: np.ndarray, P: int, D: int, qk_fp8: bool,
+                    fixed=None, tile_tokens: int = 64) -> float:
     """Bytes of K and V^T the fine kernel streams from L2 into LDS in one
-    forward: every visit of key tile j brings its 32-key halves that hold a
-    valid key (one or two), each a K half (32 keys x D, bf16 or E4M3 codes
-    plus 32 fp32 scales) and a V^T half (D x 32 keys, bf16)."""
-    H, NV, topk = sel.shape
-    halves = 1.0 + (valid > 32)
+    forward: each query block that holds a token visits every 64-slot block
+    of its key tiles (sel and fixed as for fine_flops), and a block visit
+    brings the block's 32-key halves that hold a valid key (at least one),
+    each a K half (32 keys x D, bf16 or E4M3 codes plus 32 fp32 scales) and a
+    V^T half (D x 32 keys, bf16)."""
+    H, NV, nsel = sel.shape
+    fixed = np.arange(P) if fixed is None else np.asarray(fixed, np.int64)
+    bv = _blocks(valid, tile_tokens)
+    halves = 1.0 + (bv > 32)
     kh = 32 * D * (1 if qk_fp8 else 2) + (32 * 4 if qk_fp8 else 0)
     vh = 32 * D * 2
-    per_tile = halves * (kh + vh)
-    prefix_rows = P * float(per_tile.sum()) * H
-    video_rows = NV * H * float(per_tile[:P].sum()) + float(per_tile[sel].sum())
+    per_tile = (halves * (kh + vh)).sum(axis=1)                 # [Nt]
+    qb = (bv > 0).sum(axis=1).astype(np.float64)               # query blocks with a token
+    prefix_rows = float(qb[:P].sum()) * float(per_tile.sum()) * H
+    per_row = float(per_tile[fixed].sum()) + per_tile[sel].sum(axis=2)   # [H, NV]
+    video_rows = float((per_row * qb[P:][None, :]).sum())
     return prefix_rows + video_rows
+
+
+def fixed_prefix_tiles(plan, token_tags) -> np.ndarray:
+    """Prefix tiles every video query tile visits besides its selection: all
+    of them, or with a reference selection those whose tag is not cond."""
+    P = plan.num_prefix_tiles
+    if plan.topk_ref == 0:
+        return np.arange(P)
+    perm, _, _ = plan.tables()
+    tags = np.asarray(token_tags).reshape(-1)
+    return np.array([j for j in range(P) if tags[perm[j, 0]] != 1], np.int64)
 
 
 def sources_digest(paths):
@@ -116,14 +148,17 @@ def sources_digest(paths):
     return h.hexdigest()
 
 
-def load_traffic(launches: int):
+def load_traffic(launches: int, workload: str):
     """HBM bytes per fine-attention launch (the forward's fine-branch bytes over
     its key-chunk launches) from the committed counter summary, or None if it
-    is missing or was taken on a different kernel source or launch count."""
+    is missing or was taken on a different workload, kernel source or launch
+    count."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload:
         return None
     if t.get("kernel_sources_sha256") != sources_digest(FINE_SOURCES):
         return None
@@ -141,17 +176,24 @@ def cpu_baseline(x, w, gpu_out, gpu_sel, plan, head=0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid, w.tile)
     topk = oracle.topk_count(g.NV, w.sparsity)
     t0 = time.perf_counter()
-    r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, head)
+    r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, head,
+                            ref_keep=w.ref_keep)
     t1 = time.perf_counter()
-    alg, _ = fine_flops(r.sel[None].astype(np.int64), g.valid, g.P, g.L, w.head_dim)
+    if r.ref_sel is None:
+        sel_o, fixed = r.sel, None
+    else:
+        sel_o = np.concatenate([r.ref_sel, r.sel], axis=1)
+        fixed = np.nonzero(g.tile_tag[:g.P] != oracle.COND)[0]
+    alg, _ = fine_flops(sel_o[None].astype(np.int64), g.valid, g.P, g.L, w.head_dim, fixed,
+                        g.tile_tokens)
     flops = alg + 4.0 * w.head_dim * g.Nt ** 2
     ref = oracle.round_bf16_from_f64(r.out)
     got = gpu_out[:, head, :].to("cpu").double().numpy()
     d = got - ref
-    parity = {"head": head, "sel_bit_exact": bool(np.array_equal(gpu_sel[head], r.sel)),
+    parity = {"head": head, "sel_bit_exact": bool(np.array_equal(gpu_sel[head], sel_o)),
               "max_abs": float(np.abs(d).max()),
               "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref))}
     return {"value": flops / (t1 - t0) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
@@ -165,7 +207,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="768p10s")
+    ap.add_argument("--workload", default="768p10s",
+                    help="a workload name from workloads.WORKLOADS, e.g. omniref768p10s "
+                         "(128-token tiles, reference keep 0.1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--qk-fp8", action="store_true",
                     help="time the forward with per-token FP8 (E4M3) q and k in the fine branch")
@@ -196,11 +240,12 @@ def main():
     torch.cuda.set_device(dev)
     xd = {n: x[n].to(dev) for n in ("q", "k", "v", "gate")}
     plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim, w.sparsity,
-                    qk_prep=args.qk_prep, qk_fp8=args.qk_fp8)
+                    w.tile, qk_prep=args.qk_prep, qk_fp8=args.qk_fp8, ref_keep=w.ref_keep)
     stream = torch.cuda.current_stream(dev)
     ws = plan.workspace(dev, stream.cuda_stream)
     out = torch.empty_like(xd["q"])
-    sel = torch.empty((w.heads, plan.num_video_tiles, plan.topk), dtype=torch.int32, device=dev)
+    sel = torch.empty((w.heads, plan.num_video_tiles, plan.sel_width), dtype=torch.int32,
+                      device=dev)
     io = vsa.VSA_BF16 if w.io_dtype == "bf16" else vsa.VSA_F32
     ptrs = [xd[n].data_ptr() for n in ("q", "k", "v", "gate")]
 
@@ -251,10 +296,11 @@ def main():
 
     perm, valid, _ = plan.tables()
     sel_h = sel.cpu().numpy()
+    fixed = fixed_prefix_tiles(plan, x["token_tags"])
     alg_fine, padded_fine = fine_flops(sel_h.astype(np.int64), valid, plan.num_prefix_tiles,
-                                       plan.L, w.head_dim)
+                                       plan.L, w.head_dim, fixed, plan.tile_tokens)
     kv_bytes = kv_stream_bytes(sel_h.astype(np.int64), valid, plan.num_prefix_tiles, w.head_dim,
-                               bool(args.qk_fp8))
+                               bool(args.qk_fp8), fixed, plan.tile_tokens)
     coarse_flops = 4.0 * w.head_dim * plan.num_tiles ** 2 * w.heads
     total = alg_fine + coarse_flops
     tflops = total / (ms_per_step * 1e-3) / 1e12
@@ -268,8 +314,10 @@ def main():
     fine_peak = (2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS) if args.qk_fp8
                  else PEAK_BF16_TFLOPS)
 
+    metric = METRIC if w.name == "768p10s" else (
+        f"VSA-H3 fwd ms and effective TFLOP/s (% bf16 MFMA peak) at {plan.L / 1000:.1f}k tokens")
     rec = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -286,6 +334,7 @@ def main():
             "workload": w.name, "tokens": plan.L, "heads": w.heads, "head_dim": w.head_dim,
             "prefix_tokens": w.n_prefix_tokens, "grid": list(w.grid),
             "sparsity": w.sparsity, "topk": plan.topk, "tiles": plan.num_tiles,
+            "tile": list(w.tile), "ref_keep": w.ref_keep, "topk_ref": plan.topk_ref,
             "qk_prep": bool(args.qk_prep), "qk_fp8": bool(args.qk_fp8),
             "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
             "flops_effective": total, "flops_fine_padded_tiles": padded_fine,
@@ -298,7 +347,7 @@ def main():
             "bound": "mfma", "kernel": "fine_attn_kernel",
             "achieved": round(fine_tflops, 2), "peak": fine_peak, "unit": "TFLOP/s",
             "frac": round(fine_tflops / fine_peak, 4),
-            "traffic": load_traffic(launches),
+            "traffic": load_traffic(launches, w.name),
             "launches_per_forward": launches,
             "key_chunk_tiles": plan.chunk_tiles,
             "algorithmic_flops_per_launch": alg_fine / launches,

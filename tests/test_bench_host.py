@@ -5,7 +5,7 @@ import numpy as np
 
 import bench
 import oracle
-from workloads import AUDIO, TEXT, Workload, make_layout
+from workloads import AUDIO, COND, TEXT, Workload, make_layout
 
 
 def _geometry():
@@ -65,3 +65,58 @@ def test_kv_stream_counts_one_half_for_short_tiles():
     full = bench.kv_stream_bytes(sel, np.full_like(g.valid, 64), g.P, w.head_dim, False)
     part = bench.kv_stream_bytes(sel, g.valid, g.P, w.head_dim, False)
     assert part < full
+
+
+def _wide_geometry():
+    # 128-token (4,8,4) tiles: prefix tiles of 128, 72 (one empty second
+    # block), 128 + 40 reference tokens and 30 audio tokens; a 6x10x10 grid
+    # gives video tiles of 128, 64 (empty second block) and fewer tokens.
+    w = Workload("acct128", 2, 64, "f32", ((TEXT, 200), (COND, 168), (AUDIO, 30)), (6, 10, 10),
+                 0.6, tile=(4, 8, 4), ref_keep=0.5)
+    tags, pos = make_layout(w)
+    g = oracle.geometry(tags, pos, w.grid, w.tile)
+    assert g.tile_tokens == 128 and (g.valid <= 64).any() and (g.valid <= 32).any()
+    return w, g
+
+
+def _wide_lists(g, H, topk, kr, seed):
+    rng = np.random.default_rng(seed)
+    ref = np.nonzero(g.tile_tag == COND)[0]
+    fixed = np.nonzero((g.tile_tag != COND) & (np.arange(g.Nt) < g.P))[0]
+    sel = np.stack([np.stack([np.sort(np.concatenate([
+        rng.choice(ref, kr, replace=False), rng.choice(np.arange(g.P, g.Nt), topk, replace=False)]))
+        for _ in range(g.NV)]) for _ in range(H)])
+    return sel, fixed
+
+
+def _block_visits(g, sel, fixed, h, i):
+    keys = list(range(g.Nt)) if i < g.P else [int(t) for t in fixed] + [int(t) for t in sel[h, i - g.P]]
+    for j in keys:
+        for b in range(2):
+            yield j, b
+
+
+def test_wide_fine_flops_and_kv_bytes_brute_force_over_blocks():
+    w, g = _wide_geometry()
+    topk = oracle.topk_count(g.NV, w.sparsity)
+    sel, fixed = _wide_lists(g, w.heads, topk, 1, seed=3)
+    D = w.head_dim
+    alg, padded = bench.fine_flops(sel, g.valid, g.P, g.L, D, fixed, 128)
+    bvalid = lambda j, b: int(min(max(g.valid[j] - 64 * b, 0), 64))
+    a = p = 0.0
+    kv = {False: 0, True: 0}
+    for h in range(w.heads):
+        for i in range(g.Nt):
+            for qb in range(2):
+                if bvalid(i, qb) == 0:
+                    continue          # the kernel skips a query block without rows
+                for j, b in _block_visits(g, sel, fixed, h, i):
+                    a += 4.0 * D * bvalid(i, qb) * bvalid(j, b)
+                    p += 4.0 * D * 64 * 64
+                    halves = 2 if bvalid(j, b) > 32 else 1
+                    for fp8 in (False, True):
+                        kv[fp8] += halves * (32 * D * (1 if fp8 else 2) + (128 if fp8 else 0)
+                                             + 32 * D * 2)
+    assert alg == a and padded == p
+    for fp8 in (False, True):
+        assert bench.kv_stream_bytes(sel, g.valid, g.P, D, fp8, fixed, 128) == kv[fp8]

@@ -103,29 +103,31 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Largest T with #{ok keys >= T} >= k (the k-th largest ok key), and how
-// many keys equal to T are still to be admitted.  Counts are ballots and
-// popcounts (scalar unit), not lane sums.  Every real key is nonzero (finite
-// scores map above 2^23), so candidates >= 1 never count a zero key.
+// Largest T with #{key >= T} >= k (the k-th largest key of a group), and how
+// many keys equal to T are still to be admitted.  Slots outside the group
+// hold key 0, which no candidate (>= 1) reaches: every real key is nonzero
+// (finite scores map above 2^23).  Counts are ballots and popcounts (scalar
+// unit), not lane sums.
 template <int MAXM>
-__device__ __forceinline__ void kth_key(const uint32_t (&key)[MAXM], const bool (&ok)[MAXM],
-                                        int k, uint32_t& thr, int& need) {
+__device__ __forceinline__ void kth_key(const uint32_t (&key)[MAXM], int k, uint32_t& thr,
+                                        int& need) {
   thr = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
     int c = 0;
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m)
-      c += __popcll(__builtin_amdgcn_ballot_w64(ok[m] && key[m] >= cand));
+    for (int m = 0; m < MAXM; ++m) c += __popcll(__builtin_amdgcn_ballot_w64(key[m] >= cand));
     if (c >= k) thr = cand;
   }
   int gt = 0;
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) gt += __popcll(__builtin_amdgcn_ballot_w64(ok[m] && key[m] > thr));
+  for (int m = 0; m < MAXM; ++m) gt += __popcll(__builtin_amdgcn_ballot_w64(key[m] > thr));
   need = k - gt;
 }
 
-template <int MAXM>
+// REFSEL: a reference selection (topk_ref > 0) runs as its own instance, so
+// that the registers of its second key group do not weigh on the common case.
+template <int MAXM, bool REFSEL>
 __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(
     float* __restrict__ S, int H, int Nt, int Ns, int P, int NV, int topk, float scale_log2,
     int32_t* __restrict__ sel, int nchunks, int chunk_tiles, int32_t* __restrict__ choff,
@@ -145,23 +147,25 @@ __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(
   }
 
   if (i >= P && topk > 0) {
-    // Keys of every tile; the groups are the video key tiles j in [P, Nt)
-    // and, with a reference selection, the reference tiles among 0..P-1.
-    const bool refsel = topk_ref > 0;
-    uint32_t key[MAXM];
-    bool okv[MAXM], okr[MAXM], fixed[MAXM];
+    // Keys of the two groups: the video key tiles j in [P, Nt) and, with a
+    // reference selection, the reference tiles among 0..P-1 (0 elsewhere).
+    constexpr int MR = REFSEL ? MAXM : 1;
+    uint32_t keyv[MAXM], keyr[MR];
+    bool okv[MAXM], okr[MR];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
       const int j = lane + 64 * m;
       okv[m] = j >= P && j < Nt;
-      okr[m] = refsel && j < P && kind[j] == kKindRefTile;
-      fixed[m] = refsel && j < P && !okr[m];
-      key[m] = j < Nt ? order_key(s[m]) : 0u;
+      keyv[m] = okv[m] ? order_key(s[m]) : 0u;
+      if constexpr (REFSEL) {
+        okr[m] = j < P && kind[j] == kKindRefTile;
+        keyr[m] = okr[m] ? order_key(s[m]) : 0u;
+      }
     }
     uint32_t thr_v, thr_r = 0;
     int need_v, need_r = 0;  // ties to admit, lowest index first
-    kth_key<MAXM>(key, okv, topk, thr_v, need_v);
-    if (refsel) kth_key<MAXM>(key, okr, topk_ref, thr_r, need_r);
+    kth_key<MAXM>(keyv, topk, thr_v, need_v);
+    if constexpr (REFSEL) kth_key<MAXM>(keyr, topk_ref, thr_r, need_r);
     const uint64_t below = (uint64_t(1) << lane) - 1;
     // Lane c <= nchunks also counts the entries of the fine branch's list
     // (visit with a reference selection, else sel) below c * chunk_tiles (the
@@ -169,34 +173,34 @@ __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(
     // lanes of block xm below xr.
     const int xb = min(lane * chunk_tiles, Nt);
     const int xm = xb >> 6, xr = xb & 63;
-    int below_x = refsel ? visit_len : topk;
+    int below_x = REFSEL ? visit_len : topk;
     int tie_v = 0, tie_r = 0, out_s = 0, out_l = 0;
     const size_t row = static_cast<size_t>(h) * NV + (i - P);
     int32_t* dst = sel + row * (topk_ref + topk);
-    int32_t* vdst = refsel ? visit + row * visit_len : nullptr;
+    int32_t* vdst = REFSEL ? visit + row * visit_len : nullptr;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
-      const bool tv = okv[m] && key[m] == thr_v;
+      const bool tv = okv[m] && keyv[m] == thr_v;
       const uint64_t tvmask = __ballot(tv);
       const int rank_v = tie_v + __popcll(tvmask & below);
       tie_v += __popcll(tvmask);
-      bool take = okv[m] && (key[m] > thr_v || (tv && rank_v < need_v));
-      if (refsel) {
-        const bool tr = okr[m] && key[m] == thr_r;
+      bool take = okv[m] && (keyv[m] > thr_v || (tv && rank_v < need_v));
+      uint64_t lmask;
+      if constexpr (REFSEL) {
+        const bool tr = okr[m] && keyr[m] == thr_r;
         const uint64_t trmask = __ballot(tr);
         const int rank_r = tie_r + __popcll(trmask & below);
         tie_r += __popcll(trmask);
-        take = take || (okr[m] && (key[m] > thr_r || (tr && rank_r < need_r)));
+        take = take || (okr[m] && (keyr[m] > thr_r || (tr && rank_r < need_r)));
+        // Listed: the selected tiles and the prefix tiles outside the reference group.
+        const bool listed = take || (lane + 64 * m < P && !okr[m]);
+        lmask = __ballot(listed);
+        if (listed) vdst[out_l + __popcll(lmask & below)] = lane + 64 * m;
       }
       const uint64_t omask = __ballot(take);
       if (take) dst[out_s + __popcll(omask & below)] = lane + 64 * m;
       out_s += __popcll(omask);
-      uint64_t lmask = omask;
-      if (refsel) {
-        const bool listed = take || fixed[m];
-        lmask = __ballot(listed);
-        if (listed) vdst[out_l + __popcll(lmask & below)] = lane + 64 * m;
-      }
+      if constexpr (!REFSEL) lmask = omask;
       if (m == xm) below_x = out_l + __popcll(lmask & ((uint64_t(1) << xr) - 1));
       out_l += __popcll(lmask);
     }
@@ -319,9 +323,18 @@ hipError_t launch_d(const CoarseArgs& a, hipStream_t stream) {
   // 32, then of 8) covering ceil(Nt / 64).
   const int maxm = (a.Nt + 63) / 64;
 #define VSA_TOPK(M)                                                                           \
-  hipLaunchKernelGGL((coarse_softmax_topk_kernel<M>), g2, dim3(256), 0, stream, a.scores, a.H, \
-                     a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel, a.nchunks,              \
-                     a.chunk_tiles, a.choff, a.kind, a.topk_ref, a.visit, a.visit_len)
+  do {                                                                                       \
+    if (a.topk_ref > 0)                                                                      \
+      hipLaunchKernelGGL((coarse_softmax_topk_kernel<M, true>), g2, dim3(256), 0, stream,      \
+                         a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel,      \
+                         a.nchunks, a.chunk_tiles, a.choff, a.kind, a.topk_ref, a.visit,       \
+                         a.visit_len);                                                       \
+    else                                                                                     \
+      hipLaunchKernelGGL((coarse_softmax_topk_kernel<M, false>), g2, dim3(256), 0, stream,     \
+                         a.scores, a.H, a.Nt, a.Ns, a.P, a.NV, a.topk, scale_log2, a.sel,      \
+                         a.nchunks, a.chunk_tiles, a.choff, a.kind, a.topk_ref, a.visit,       \
+                         a.visit_len);                                                       \
+  } while (0)
   if (maxm <= 4) VSA_TOPK(4);
   else if (maxm <= 8) VSA_TOPK(8);
   else if (maxm <= 12) VSA_TOPK(12);
