@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "VSA-H3 fwd ms and effective TFLOP/s (% bf16 MFMA peak) at 73.6k tokens"
 FINE_SOURCES = ["video_dit_block_amd/csrc/fine_attn.hip", "video_dit_block_amd/csrc/device.hpp",
                 "video_dit_block_amd/csrc/kernels.hpp", "video_dit_block_amd/csrc/plan.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_768p10s_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_{workload}_traffic.json")
 
 
 def log(*a):
@@ -154,7 +154,7 @@ def load_traffic(launches: int, workload: str):
     is missing or was taken on a different workload, kernel source or launch
     count."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload=workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
