@@ -17,10 +17,11 @@
 // Design (gfx950, wave64):
 //   - tiles hold 64 or 128 tokens and are handled as 64-slot blocks (a
 //     128-token tile is two consecutive blocks);
-//   - one block of 2 waves per (head, query block); wave w owns query rows
-//     32w..32w+31 of the 64-row block, gathered straight from the packed
-//     [L][H][D] input through the block's slot table into MFMA operand
-//     registers;
+//   - one workgroup of 2 waves per (head, query block), or with 128-token
+//     tiles and bf16 q/k one of 4 waves per (head, query tile), so that the
+//     tile's two query blocks share every K/V load; wave w owns query rows
+//     32w..32w+31, gathered straight from the packed [L][H][D] input through
+//     the slot table into MFMA operand registers;
 //   - the visit list is ascending (prefix tiles 0..P-1, or the listed ones,
 //     then the selected video tiles) and visits each tile's blocks in order;
 //     a tile's first block always holds a token, so every row has a finite
@@ -31,7 +32,8 @@
 //     global->LDS loads (global_load_lds_dwordx4, no register staging).  A
 //     slot is refilled with the next tile's half as soon as both waves have
 //     read it, so each load has about three quarters of an iteration to land
-//     (32 KB of LDS per block, four blocks per CU);
+//     (32 KB of LDS per workgroup: four two-wave or two four-wave
+//     workgroups per CU);
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so
 //     each lane holds one query column), online softmax in fp32 via exp2 with
 //     the 1/sqrt(D) scale folded into log2 units; the running max is raised
@@ -188,8 +190,10 @@ __device__ __forceinline__ void load_f32x8(const TIO* p, float v[8]) {
   IoOps<TIO>::load4(p + 4, v + 4);
 }
 
-template <typename TIO, int D, bool QK8>
-__global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
+// NW waves per block own NW * 32 query rows: 2 (a 64-slot block) or 4 (a
+// whole 128-token tile, whose two blocks share every K/V load).
+template <typename TIO, int D, bool QK8, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
                                                           const int32_t* __restrict__ valid,
                                                           const int32_t* __restrict__ list,
                                                           const int32_t* __restrict__ choff,
@@ -200,8 +204,11 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   constexpr int KH_BYTES = 32 * KROWB;           // one 32-key half of a K tile
   constexpr int VH_BYTES = 64 * D;               // one 32-key half of a V^T tile: D rows of 64 B
   constexpr int V_TILE = 2 * VH_BYTES;
-  constexpr int KH_LOADS = KH_BYTES / 1024 / 2;  // 1 KB DMA loads per wave per K half
-  constexpr int VH_LOADS = VH_BYTES / 1024 / 2;  // the same per V^T half
+  static_assert(NW == 2 || (NW == 4 && !QK8), "four waves only with bf16 q/k");
+  constexpr int KH_LOADS = KH_BYTES / 1024 / NW;  // 1 KB DMA loads per wave per K half
+  constexpr int VH_LOADS = VH_BYTES / 1024 / NW;  // the same per V^T half
+  static_assert(KH_LOADS * NW * 1024 == KH_BYTES && VH_LOADS * NW * 1024 == VH_BYTES,
+                "a half splits evenly over the waves");
   constexpr int NK64 = D / 64;                   // FP8 MFMA steps of 64 channels
   constexpr int NCK = D / 16;                    // QK contraction steps
   constexpr int NB = D / 32;                     // O^T blocks of 32 channels
@@ -223,14 +230,19 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   // Tiles are 1 << bsh blocks of 64 slots; the block is the unit of work.
   const int bsh = a.bsh, Nb = Nt << bsh, Pvis = a.Pvis;
 
-  int hd, ib;  // head, query block
+  // A query item is 1 << ish blocks: one block with two waves, a whole
+  // 128-token tile with four.
+  constexpr int ish = NW == 4 ? 1 : 0;
+  int hd, ib;  // head, first query block of the item
   if (a.nchunks > 1)
-    decode_item_chunked(blockIdx.x, H, Nb, hd, ib);
+    decode_item_chunked(blockIdx.x, H, Nb >> ish, hd, ib);
   else
-    decode_item(blockIdx.x, H, P << bsh, NV << bsh, hd, ib);
+    decode_item(blockIdx.x, H, (P << bsh) >> ish, (NV << bsh) >> ish, hd, ib);
+  ib <<= ish;
   const int i = ib >> bsh;  // query tile
+  const int nrows = NW == 4 ? valid[ib] + valid[ib + 1] : valid[ib];
   // The second block of a 128-token tile with at most 64 tokens has no rows.
-  if (valid[ib] == 0) return;
+  if (nrows == 0) return;
 
   // Visit list of tiles: prefix tiles 0..Pvis-1 then the query tile's row of
   // the list (all tiles for a prefix query tile), ascending; every tile is
@@ -260,9 +272,9 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   // Query fragment: B operand of S^T = K Q^T (column = query, k = channel).
   const TIO* q = static_cast<const TIO*>(a.q);
   const int pr = a.perm[static_cast<size_t>(ib) * 64 + 32 * w + l32];
-  // A wave whose 32 query rows are all pad slots (the second half of a block
-  // with at most 32 valid tokens) only takes part in the loads and barriers.
-  const bool active = 32 * w < valid[ib];
+  // A wave whose 32 query rows are all pad slots (the end of an item with
+  // fewer valid tokens) only takes part in the loads and barriers.
+  const bool active = 32 * w < nrows;
   // Rows come from the packed input, or from the tile-ordered copy that the
   // gather wrote after QK-norm and RoPE (pad rows are zero there).
   bf16x8 qf[QK8 ? 1 : NCK];
@@ -757,17 +769,27 @@ __global__ __launch_bounds__(128, 2) void fine_attn_kernel(FineArgs a,
   }
 }
 
-template <typename TIO, int D, bool QK8>
-hipError_t launch_q(const FineArgs& a, hipStream_t stream) {
-  const int blocks = a.H * (a.Nt << a.bsh);
+template <typename TIO, int D, bool QK8, int NW>
+hipError_t launch_w(const FineArgs& a, hipStream_t stream) {
+  // One block per query item: a 64-slot block (NW 2) or a 128-token tile (NW 4).
+  const int blocks = a.H * ((a.Nt << a.bsh) >> (NW == 4 ? 1 : 0));
   const int nchunks = a.nchunks > 1 ? a.nchunks : 1;
   for (int c = 0; c < nchunks; ++c) {
-    hipLaunchKernelGGL((fine_attn_kernel<TIO, D, QK8>), dim3(blocks), dim3(128), 0, stream, a,
-                       a.valid, a.list, a.choff, a.state, c);
+    hipLaunchKernelGGL((fine_attn_kernel<TIO, D, QK8, NW>), dim3(blocks), dim3(64 * NW), 0,
+                       stream, a, a.valid, a.list, a.choff, a.state, c);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+template <typename TIO, int D, bool QK8>
+hipError_t launch_q(const FineArgs& a, hipStream_t stream) {
+  // 128-token tiles with bf16 q/k: the tile's two query blocks share one
+  // block of four waves, and so every K/V load.
+  if constexpr (!QK8)
+    if (a.bsh == 1) return launch_w<TIO, D, false, 4>(a, stream);
+  return launch_w<TIO, D, QK8, 2>(a, stream);
 }
 
 template <typename TIO, int D>
