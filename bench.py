@@ -90,19 +90,18 @@ def fine_flops(sel: np.ndarray, valid: np.ndarray, P: int, L: int, D: int, fixed
     FLOPs the MFMA executes, for one forward.  sel: [H, NV, n] selected key
     tiles (global ids) of each video query tile; fixed: the prefix tiles every
     video query tile visits besides them (default: all P prefix tiles).  The
-    kernel works on 64-slot blocks: each query block that holds a token visits
-    every block of each listed key tile."""
+    kernel works on 64-slot blocks: each query block that holds a token meets
+    every block that holds a key in each listed key tile."""
     H, NV, nsel = sel.shape
     fixed = np.arange(P) if fixed is None else np.asarray(fixed, np.int64)
     n = valid.astype(np.float64)
-    Nt = n.shape[0]
     per_row = float(n[fixed].sum()) + n[sel].sum(axis=2)      # [H, NV] keys per video query
     video = float((per_row * n[P:][None, :]).sum())
     prefix = float(n[:P].sum()) * L * H
     alg = 4.0 * D * (video + prefix)
-    qb = (_blocks(valid, tile_tokens) > 0).sum(axis=1)          # query blocks with a token
-    kb = tile_tokens // 64
-    pairs = H * (float(qb[P:].sum()) * (len(fixed) + nsel) + float(qb[:P].sum()) * Nt) * kb
+    nb = (_blocks(valid, tile_tokens) > 0).sum(axis=1).astype(np.float64)   # blocks with a token
+    keys_video = float(nb[fixed].sum()) + nb[sel].sum(axis=2)               # [H, NV]
+    pairs = float((keys_video * nb[P:][None, :]).sum()) + H * float(nb[:P].sum()) * float(nb.sum())
     padded = 4.0 * D * 64 * 64 * pairs
     return alg, padded
 
@@ -110,19 +109,24 @@ def fine_flops(sel: np.ndarray, valid: np.ndarray, P: int, L: int, D: int, fixed
 def kv_stream_bytes(sel: np.ndarray, valid: np.ndarray, P: int, D: int, qk_fp8: bool,
                     fixed=None, tile_tokens: int = 64) -> float:
     """Bytes of K and V^T the fine kernel streams from L2 into LDS in one
-    forward: each query block that holds a token visits every 64-slot block
-    of its key tiles (sel and fixed as for fine_flops), and a block visit
-    brings the block's 32-key halves that hold a valid key (at least one),
-    each a K half (32 keys x D, bf16 or E4M3 codes plus 32 fp32 scales) and a
-    V^T half (D x 32 keys, bf16)."""
+    forward: each query item visits every 64-slot block that holds a key in
+    its key tiles (sel and fixed as for fine_flops), and a block visit brings
+    the block's 32-key halves that hold a valid key, each a K half (32 keys x
+    D, bf16 or E4M3 codes plus 32 fp32 scales) and a V^T half (D x 32 keys,
+    bf16).  A query item is a whole 128-token tile with bf16 q/k (its two
+    query blocks share one workgroup), else a query block that holds a
+    token."""
     H, NV, nsel = sel.shape
     fixed = np.arange(P) if fixed is None else np.asarray(fixed, np.int64)
     bv = _blocks(valid, tile_tokens)
-    halves = 1.0 + (bv > 32)
+    halves = (bv > 0) * (1.0 + (bv > 32))
     kh = 32 * D * (1 if qk_fp8 else 2) + (32 * 4 if qk_fp8 else 0)
     vh = 32 * D * 2
     per_tile = (halves * (kh + vh)).sum(axis=1)                 # [Nt]
-    qb = (bv > 0).sum(axis=1).astype(np.float64)               # query blocks with a token
+    if tile_tokens == 128 and not qk_fp8:
+        qb = np.ones(bv.shape[0])                               # one item per query tile
+    else:
+        qb = (bv > 0).sum(axis=1).astype(np.float64)           # query blocks with a token
     prefix_rows = float(qb[:P].sum()) * float(per_tile.sum()) * H
     per_row = float(per_tile[fixed].sum()) + per_tile[sel].sum(axis=2)   # [H, NV]
     video_rows = float((per_row * qb[P:][None, :]).sum())

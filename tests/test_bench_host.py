@@ -97,7 +97,12 @@ def _block_visits(g, sel, fixed, h, i):
 
 
 def test_wide_fine_flops_and_kv_bytes_brute_force_over_blocks():
+    """A query block without rows does no work and a key block without keys
+    is stepped over.  With bf16 q/k both query blocks of a 128-token tile
+    share one workgroup and so one K/V stream; with FP8 q/k each query block
+    that holds a row streams its own."""
     w, g = _wide_geometry()
+    assert (g.valid[g.P:] <= 64).any()
     topk = oracle.topk_count(g.NV, w.sparsity)
     sel, fixed = _wide_lists(g, w.heads, topk, 1, seed=3)
     D = w.head_dim
@@ -105,18 +110,20 @@ def test_wide_fine_flops_and_kv_bytes_brute_force_over_blocks():
     bvalid = lambda j, b: int(min(max(g.valid[j] - 64 * b, 0), 64))
     a = p = 0.0
     kv = {False: 0, True: 0}
+    kv_half = {fp8: 32 * D * (1 if fp8 else 2) + (128 if fp8 else 0) + 32 * D * 2
+               for fp8 in (False, True)}
     for h in range(w.heads):
         for i in range(g.Nt):
+            visits = [(j, b) for j, b in _block_visits(g, sel, fixed, h, i) if bvalid(j, b) > 0]
+            tile_bytes = sum(2 if bvalid(j, b) > 32 else 1 for j, b in visits)
+            kv[False] += tile_bytes * kv_half[False]            # once per query tile
             for qb in range(2):
                 if bvalid(i, qb) == 0:
-                    continue          # the kernel skips a query block without rows
-                for j, b in _block_visits(g, sel, fixed, h, i):
+                    continue
+                kv[True] += tile_bytes * kv_half[True]          # once per query block
+                for j, b in visits:
                     a += 4.0 * D * bvalid(i, qb) * bvalid(j, b)
                     p += 4.0 * D * 64 * 64
-                    halves = 2 if bvalid(j, b) > 32 else 1
-                    for fp8 in (False, True):
-                        kv[fp8] += halves * (32 * D * (1 if fp8 else 2) + (128 if fp8 else 0)
-                                             + 32 * D * 2)
     assert alg == a and padded == p
     for fp8 in (False, True):
         assert bench.kv_stream_bytes(sel, g.valid, g.P, D, fp8, fixed, 128) == kv[fp8]

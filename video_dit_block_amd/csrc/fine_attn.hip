@@ -23,10 +23,10 @@
 //     32w..32w+31, gathered straight from the packed [L][H][D] input through
 //     the slot table into MFMA operand registers;
 //   - the visit list is ascending (prefix tiles 0..P-1, or the listed ones,
-//     then the selected video tiles) and visits each tile's blocks in order;
-//     a tile's first block always holds a token, so every row has a finite
-//     running max before a block without valid keys (the second block of a
-//     short 128-token tile) can come up;
+//     then the selected video tiles) and visits each tile's blocks in order,
+//     stepping over a block without valid keys (the second block of a
+//     128-token tile with at most 64 tokens); a tile's first block always
+//     holds a token, so every row starts from a finite running max;
 //   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
 //     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
 //     global->LDS loads (global_load_lds_dwordx4, no register staging).  A
@@ -191,8 +191,9 @@ __device__ __forceinline__ void load_f32x8(const TIO* p, float v[8]) {
 }
 
 // NW waves per block own NW * 32 query rows: 2 (a 64-slot block) or 4 (a
-// whole 128-token tile, whose two blocks share every K/V load).
-template <typename TIO, int D, bool QK8, int NW>
+// whole 128-token tile, whose two blocks share every K/V load).  A tile is
+// 1 << BSH blocks (BSH 0: 64-token tiles, 1: 128-token tiles).
+template <typename TIO, int D, bool QK8, int NW, int BSH>
 __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
                                                           const int32_t* __restrict__ valid,
                                                           const int32_t* __restrict__ list,
@@ -204,7 +205,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   constexpr int KH_BYTES = 32 * KROWB;           // one 32-key half of a K tile
   constexpr int VH_BYTES = 64 * D;               // one 32-key half of a V^T tile: D rows of 64 B
   constexpr int V_TILE = 2 * VH_BYTES;
-  static_assert(NW == 2 || (NW == 4 && !QK8), "four waves only with bf16 q/k");
+  static_assert(NW == 2 || (NW == 4 && !QK8 && BSH == 1),
+                "four waves only for 128-token tiles with bf16 q/k");
   constexpr int KH_LOADS = KH_BYTES / 1024 / NW;  // 1 KB DMA loads per wave per K half
   constexpr int VH_LOADS = VH_BYTES / 1024 / NW;  // the same per V^T half
   static_assert(KH_LOADS * NW * 1024 == KH_BYTES && VH_LOADS * NW * 1024 == VH_BYTES,
@@ -228,7 +230,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   const int l32 = lane & 31;
   const int H = a.H, Nt = a.Nt, P = a.P, NV = a.NV;
   // Tiles are 1 << bsh blocks of 64 slots; the block is the unit of work.
-  const int bsh = a.bsh, Nb = Nt << bsh, Pvis = a.Pvis;
+  constexpr int bsh = BSH;
+  const int Nb = Nt << bsh, Pvis = a.Pvis;
 
   // A query item is 1 << ish blocks: one block with two waves, a whole
   // 128-token tile with four.
@@ -631,12 +634,20 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   // V^T half 0 of t + 1; each wait below counts the loads issued after the
   // half it needs.
   const f32x16 kNone = {};
-  for (int it = beg; it < end; ++it) {
+  for (int it = beg; it < end;) {
     const bool has1 = nj > 32;   // the second half holds a valid key
     // The last iteration re-requests its own tile, so that every iteration
-    // issues the same loads and the wait counts stay exact.
-    const int jn = it + 1 < end ? tile_at(it + 1) : j;
-    const int njn = valid[jn];
+    // issues the same loads and the wait counts stay exact.  A block without
+    // valid keys (only ever the second block of a short 128-token tile) is
+    // stepped over.
+    int itn = it + 1;
+    int jn = itn < end ? tile_at(itn) : j;
+    int njn = valid[jn];
+    if (bsh > 0 && njn == 0) {
+      ++itn;
+      jn = itn < end ? tile_at(itn) : j;
+      njn = valid[jn];
+    }
 
     // K half 0 of t landed; every wave is done with V^T half 1 of t - 1.
     wait_vm(ck(nj, 1) + cv(nj, 0));
@@ -719,6 +730,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
     }
     j = jn;
     nj = njn;
+    it = itn;
   }
   // No global->LDS load may still be in flight when the block's LDS is released.
   __builtin_amdgcn_s_waitcnt(kWaitVm);
@@ -769,13 +781,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   }
 }
 
-template <typename TIO, int D, bool QK8, int NW>
+template <typename TIO, int D, bool QK8, int NW, int BSH>
 hipError_t launch_w(const FineArgs& a, hipStream_t stream) {
   // One block per query item: a 64-slot block (NW 2) or a 128-token tile (NW 4).
-  const int blocks = a.H * ((a.Nt << a.bsh) >> (NW == 4 ? 1 : 0));
+  const int blocks = a.H * ((a.Nt << BSH) >> (NW == 4 ? 1 : 0));
   const int nchunks = a.nchunks > 1 ? a.nchunks : 1;
   for (int c = 0; c < nchunks; ++c) {
-    hipLaunchKernelGGL((fine_attn_kernel<TIO, D, QK8, NW>), dim3(blocks), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((fine_attn_kernel<TIO, D, QK8, NW, BSH>), dim3(blocks), dim3(64 * NW), 0,
                        stream, a, a.valid, a.list, a.choff, a.state, c);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -785,11 +797,13 @@ hipError_t launch_w(const FineArgs& a, hipStream_t stream) {
 
 template <typename TIO, int D, bool QK8>
 hipError_t launch_q(const FineArgs& a, hipStream_t stream) {
+  if (a.bsh == 0) return launch_w<TIO, D, QK8, 2, 0>(a, stream);
   // 128-token tiles with bf16 q/k: the tile's two query blocks share one
   // block of four waves, and so every K/V load.
-  if constexpr (!QK8)
-    if (a.bsh == 1) return launch_w<TIO, D, false, 4>(a, stream);
-  return launch_w<TIO, D, QK8, 2>(a, stream);
+  if constexpr (QK8)
+    return launch_w<TIO, D, true, 2, 1>(a, stream);
+  else
+    return launch_w<TIO, D, false, 4, 1>(a, stream);
 }
 
 template <typename TIO, int D>
