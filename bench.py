@@ -113,9 +113,9 @@ def kv_stream_bytes(sel: np.ndarray, valid: np.ndarray, P: int, D: int, qk_fp8: 
     its key tiles (sel and fixed as for fine_flops), and a block visit brings
     the block's 32-key halves that hold a valid key, each a K half (32 keys x
     D, bf16 or E4M3 codes plus 32 fp32 scales) and a V^T half (D x 32 keys,
-    bf16).  A query item is a whole 128-token tile with bf16 q/k (its two
-    query blocks share one workgroup), else a query block that holds a
-    token."""
+    bf16).  A query item is a whole 128-token tile (its two query blocks
+    share one workgroup), except with FP8 keys at head_dim 64, and with
+    64-token tiles a query block."""
     H, NV, nsel = sel.shape
     fixed = np.arange(P) if fixed is None else np.asarray(fixed, np.int64)
     bv = _blocks(valid, tile_tokens)
@@ -123,7 +123,7 @@ def kv_stream_bytes(sel: np.ndarray, valid: np.ndarray, P: int, D: int, qk_fp8: 
     kh = 32 * D * (1 if qk_fp8 else 2) + (32 * 4 if qk_fp8 else 0)
     vh = 32 * D * 2
     per_tile = (halves * (kh + vh)).sum(axis=1)                 # [Nt]
-    if tile_tokens == 128 and not qk_fp8:
+    if tile_tokens == 128 and not (qk_fp8 and D == 64):
         qb = np.ones(bv.shape[0])                               # one item per query tile
     else:
         qb = (bv > 0).sum(axis=1).astype(np.float64)           # query blocks with a token

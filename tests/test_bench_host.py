@@ -98,9 +98,9 @@ def _block_visits(g, sel, fixed, h, i):
 
 def test_wide_fine_flops_and_kv_bytes_brute_force_over_blocks():
     """A query block without rows does no work and a key block without keys
-    is stepped over.  With bf16 q/k both query blocks of a 128-token tile
-    share one workgroup and so one K/V stream; with FP8 q/k each query block
-    that holds a row streams its own."""
+    is stepped over.  Both query blocks of a 128-token tile share one
+    workgroup and so one K/V stream, except with FP8 keys at head_dim 64,
+    where each query block that holds a row streams its own."""
     w, g = _wide_geometry()
     assert (g.valid[g.P:] <= 64).any()
     topk = oracle.topk_count(g.NV, w.sparsity)
@@ -127,3 +127,6 @@ def test_wide_fine_flops_and_kv_bytes_brute_force_over_blocks():
     assert alg == a and padded == p
     for fp8 in (False, True):
         assert bench.kv_stream_bytes(sel, g.valid, g.P, D, fp8, fixed, 128) == kv[fp8]
+    # at head_dim 128 FP8 keys split over four waves too: once per query tile
+    kv128 = kv[False] // kv_half[False] * (32 * 128 + 128 + 32 * 128 * 2)
+    assert bench.kv_stream_bytes(sel, g.valid, g.P, 128, True, fixed, 128) == kv128

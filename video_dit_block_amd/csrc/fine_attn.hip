@@ -205,8 +205,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   constexpr int KH_BYTES = 32 * KROWB;           // one 32-key half of a K tile
   constexpr int VH_BYTES = 64 * D;               // one 32-key half of a V^T tile: D rows of 64 B
   constexpr int V_TILE = 2 * VH_BYTES;
-  static_assert(NW == 2 || (NW == 4 && !QK8 && BSH == 1),
-                "four waves only for 128-token tiles with bf16 q/k");
+  static_assert(NW == 2 || (NW == 4 && BSH == 1), "four waves only for 128-token tiles");
   constexpr int KH_LOADS = KH_BYTES / 1024 / NW;  // 1 KB DMA loads per wave per K half
   constexpr int VH_LOADS = VH_BYTES / 1024 / NW;  // the same per V^T half
   static_assert(KH_LOADS * NW * 1024 == KH_BYTES && VH_LOADS * NW * 1024 == VH_BYTES,
@@ -372,7 +371,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
 // memory clobber keeps the compiler from moving memory accesses across it.
 #define VSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 // Half B of K tile J into slot SLOT: KH_LOADS loads per wave and, with QK8,
-// one load of the wave's 16 per-key scales (lanes 4..63 repeat lanes 0..3).
+// one load of 16 per-key scales by each of waves 0 and 1 (lanes 4..63 repeat
+// lanes 0..3).
 // Pad rows are zero in memory, so a loaded half holds no stale data; a half
 // without valid keys is neither loaded nor read.
 #define VSA_LOAD_KH(SLOT, J, B)                                                               \
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
           (gbl_void*)(src_ + kbase + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64),                  \
           (lds_void*)((SLOT) + x_ * 1024), 16, 0, 0);                                          \
     }                                                                                          \
-    if (QK8)                                                                                   \
+    if (QK8 && w < 2)                                                                          \
       __builtin_amdgcn_global_load_lds(                                                        \
           (gbl_void*)(ksh + static_cast<size_t>(J) * 256 + 128 * (B) + 64 * w + 16 * (lane & 3)), \
           (lds_void*)((SLOT) + KH_BYTES + 1024 * w), 16, 0, 0);                                \
@@ -400,10 +400,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
     }                                                                                          \
   }
   // Loads this wave issues for half b of a tile with n valid keys.
-  constexpr int CK = KH_LOADS + (QK8 ? 1 : 0);
+  constexpr int CKMAX = KH_LOADS + (QK8 ? 1 : 0);
+  const int CK = KH_LOADS + (QK8 && w < 2 ? 1 : 0);
   constexpr int CV = VH_LOADS;
-  static_assert(2 * (CK > CV ? CK : CV) <= 8, "wait counts above 8");
-  auto ck = [](int n, int b) -> int { return n > 32 * b ? CK : 0; };
+  static_assert(2 * (CKMAX > CV ? CKMAX : CV) <= 8, "wait counts above 8");
+  auto ck = [CK](int n, int b) -> int { return n > 32 * b ? CK : 0; };
   auto cv = [](int n, int b) -> int { return n > 32 * b ? CV : 0; };
   // Wait until at most n of this wave's loads are in flight.
   auto wait_vm = [](int n) {
@@ -798,12 +799,13 @@ hipError_t launch_w(const FineArgs& a, hipStream_t stream) {
 template <typename TIO, int D, bool QK8>
 hipError_t launch_q(const FineArgs& a, hipStream_t stream) {
   if (a.bsh == 0) return launch_w<TIO, D, QK8, 2, 0>(a, stream);
-  // 128-token tiles with bf16 q/k: the tile's two query blocks share one
-  // block of four waves, and so every K/V load.
-  if constexpr (QK8)
+  // 128-token tiles: the tile's two query blocks share one block of four
+  // waves, and so every K/V load -- unless a K half (FP8 codes at head_dim
+  // 64: 2 KB) does not split into 1 KB loads for four waves.
+  if constexpr (QK8 && D == 64)
     return launch_w<TIO, D, true, 2, 1>(a, stream);
   else
-    return launch_w<TIO, D, false, 4, 1>(a, stream);
+    return launch_w<TIO, D, QK8, 4, 1>(a, stream);
 }
 
 template <typename TIO, int D>
