@@ -473,7 +473,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   // The MFMA operands are read from LDS kAhead steps ahead of their use.
   constexpr int kQkSteps = QK8 ? NK64 : NCK;
   constexpr int kPvSteps = 2 * NB;
-  constexpr int kAhead = 2;
+  constexpr int kAhead = 3;
   typedef typename std::conditional<QK8, i32x8, bf16x8>::type QkOp;
 
   // LDS operand of Q.K step k of half b (lane row l32 of the half's keys).
