@@ -160,7 +160,8 @@ vsa_status vsa_h3_plan_info(const vsa_h3_plan* plan, vsa_h3_info* out);
  * sum and unnormalised output of every query row pass between launches
  * through the workspace, in fp32.
  *   chunk_tiles  0 picks the default (chunks of at most 10 MiB of K+V per
- *                head, balanced; with FP8 q/k the keys count one byte per
+ *                head with 64-token tiles, 32 MiB with 128-token tiles,
+ *                balanced; with FP8 q/k the keys count one byte per
  *                element); otherwise the chunk length in key tiles.
  * The workspace size changes: call before sizing and uploading a workspace.
  * VSA_E_ARG if chunk_tiles < 0 or if it gives more than 63 chunks. */

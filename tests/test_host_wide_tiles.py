@@ -107,6 +107,8 @@ def test_wide_workspace_regions_sized_and_disjoint():
     for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
         assert a0 % 256 == 0 and a1 <= b0
     assert spans[-1][1] <= lo.total == p.workspace_bytes
-    # a 128-token tile's K+V is 64 KiB at head_dim 128: at most 160 tiles per 10 MiB chunk
-    assert p.chunk_tiles * 128 * D * 4 <= 10 << 20
+    # a 128-token tile's K+V is 64 KiB at head_dim 128: at most 512 tiles per
+    # 32 MiB chunk, balanced: 670 tiles in 2 chunks of 335
+    assert (p.chunk_tiles, p.num_chunks) == (335, 2)
+    assert p.chunk_tiles * 128 * D * 4 <= 32 << 20
     assert (p.num_chunks - 1) * p.chunk_tiles < Nt <= p.num_chunks * p.chunk_tiles

@@ -98,7 +98,8 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
     // in bf16, or FP8 codes, plus bf16 V^T), then balanced over the chunks.
     const uint64_t tile_bytes =
         uint64_t(plan->tile_tokens) * plan->head_dim * (plan->qk_fp8 ? 3 : 4);
-    const int64_t cap = static_cast<int64_t>(kChunkBytes / tile_bytes);
+    const uint64_t budget = plan->tile_tokens == 128 ? kChunkBytesWide : kChunkBytes;
+    const int64_t cap = static_cast<int64_t>(budget / tile_bytes);
     const int64_t nc = std::max<int64_t>(1, ceil_div(Nt, cap));
     ch = std::max<int64_t>(1, ceil_div(Nt, nc));
   } else {

@@ -23,6 +23,13 @@ constexpr int kMaxKeyChunks = 63;      // chunk boundaries one wave writes per q
 // 128- to 320-tile chunks measured alike on random selections and larger
 // chunks did better on spatially smooth ones.
 constexpr uint64_t kChunkBytes = uint64_t(10) << 20;
+// The same budget for 128-token tiles.  Their four-wave workgroups stream
+// every K/V block once for 128 query rows, so the L2 hit rate matters less
+// than the running-state round trips between launches.  Chunks are sized so
+// that the eight XCDs' current chunks together fill the 256 MiB Infinity
+// Cache.  On the 77,696-token OmniRef layout, chunks of 335 tiles (2
+// launches) measured 4 % faster than chunks within 10 MiB (5 launches).
+constexpr uint64_t kChunkBytesWide = uint64_t(32) << 20;
 
 struct Layout {
   uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, qt, kt8, kscale,
