@@ -170,6 +170,32 @@ def test_omniref_small_fp8_qk_parity():
     wide_check(w, make_inputs(w, seed=2), qk_fp8=True)
 
 
+FP8_WIDE = [
+    # FP8 keys at head_dim 64 do not split over four waves: two-wave blocks
+    ("d64_bf16_keep04", Workload("f64", 3, 64, "bf16", ((TEXT, 90), (COND, 300), (AUDIO, 20)),
+                                 (6, 16, 12), 0.6, tile=(4, 8, 4), ref_keep=0.4), 0),
+    ("d64_f32_chunked", Workload("f64c", 2, 64, "f32", ((COND, 200), (TEXT, 64)), (9, 8, 12),
+                                 0.5, tile=(8, 4, 4), ref_keep=0.5), 3),
+    ("d128_f32_keep1", Workload("f128", 2, 128, "f32", ((TEXT, 100), (AUDIO, 70)), (6, 9, 8),
+                                0.5, tile=(2, 8, 8)), 0),
+    ("d128_bf16_chunked", Workload("f128c", 4, 128, "bf16", ((TEXT, 64), (COND, 400)),
+                                   (10, 16, 8), 0.7, tile=(4, 8, 4), ref_keep=0.3), 4),
+]
+
+
+@pytest.mark.parametrize("name,w,ch", FP8_WIDE, ids=[f[0] for f in FP8_WIDE])
+def test_wide_fp8_qk_instances(name, w, ch):
+    """FP8 q/k on 128-token tiles in each kernel instance: two-wave blocks at
+    head_dim 64, four-wave tiles at 128, both I/O types, one and several key
+    chunks."""
+    say(f"case {name}: L={w.L} {w.io_dtype} D={w.head_dim} tile={w.tile} keep={w.ref_keep} "
+        f"chunk_tiles={ch}")
+    out, _, plan, _ = wide_check(w, make_inputs(w, seed=12, video_order="shuffled"),
+                                 qk_fp8=True, chunk_tiles=ch)
+    if ch:
+        assert plan.num_chunks > 1
+
+
 def test_wide_tiles_sparsity0_keep1_equals_dense_sdpa():
     w = Workload("dense", 2, 64, "f32", ((TEXT, 70), (COND, 140)), (6, 9, 8), 0.0,
                  tile=(4, 8, 4))
