@@ -46,14 +46,15 @@ def run(x, grid, sparsity, dev="cuda", plan=None, qk_fp8=False, chunk_tiles=0,
     return out, sel, plan, ws
 
 
-def run_qk_prep(x, prep, grid, sparsity, dev="cuda", plan=None, chunk_tiles=0):
+def run_qk_prep(x, prep, grid, sparsity, dev="cuda", plan=None, chunk_tiles=0,
+                tile=(4, 4, 4), ref_keep=1.0):
     """GPU forward with QK-norm + RoPE through the C ABI.  Returns (out, sel, plan, ws)."""
     xd = {k: x[k].to(dev) for k in ("q", "k", "v", "gate")}
     pd = {k: prep[k].to(dev) for k in ("q_weight", "k_weight", "cos", "sin")}
     L, H, D = xd["q"].shape
     if plan is None:
-        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity,
-                        chunk_tiles=chunk_tiles, qk_prep=True)
+        plan = vsa.Plan(x["token_tags"], x["position_ids"], grid, H, D, sparsity, tile,
+                        chunk_tiles=chunk_tiles, qk_prep=True, ref_keep=ref_keep)
     out, sel = vsa.forward_qk_prep(xd["q"], xd["k"], xd["v"], xd["gate"], pd["q_weight"],
                                    pd["k_weight"], prep["eps"], pd["cos"], pd["sin"], plan=plan,
                                    return_sel=True)

@@ -14,9 +14,9 @@ import torch
 
 import oracle
 import video_dit_block_amd as vsa
-from tests.gpu_helpers import (assert_close, errors, intermediates, out_f64, require_gpu, run,
-                               say)
-from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs
+from tests.gpu_helpers import (assert_close, errors, intermediates, oracle_prep, out_f64,
+                               require_gpu, run, run_qk_prep, say)
+from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs, make_qk_prep_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -215,6 +215,75 @@ def test_fp8_zero_query_rows_in_partial_tiles():
     x = make_inputs(w, seed=8)
     x["q"][::7] = 0
     wide_check(w, x, qk_fp8=True)
+
+
+WIDE_PREP = [
+    Workload("prep_d128_keep03", 4, 128, "bf16", ((TEXT, 90), (COND, 300), (AUDIO, 40)),
+             (6, 16, 12), 0.6, tile=(4, 8, 4), ref_keep=0.3),
+    Workload("prep_d64_f32", 2, 64, "f32", ((COND, 150), (TEXT, 64)), (9, 8, 8), 0.5,
+             tile=(8, 4, 4), ref_keep=0.6),
+]
+
+
+@pytest.mark.parametrize("w", WIDE_PREP, ids=[w.name for w in WIDE_PREP])
+def test_wide_tiles_with_qk_norm_rope(w):
+    """QK-norm + RoPE fused into the gather of 128-token tiles: Qt and Kt per
+    64-slot block bit-exact, pooled values over all 128 slots, selection with
+    reference keep, and the output."""
+    say(f"case {w.name} + qk prep: L={w.L} {w.io_dtype} D={w.head_dim} tile={w.tile}")
+    x = make_inputs(w, seed=14, video_order="shuffled")
+    prep = make_qk_prep_inputs(w, x["position_ids"], seed=14)
+    out, sel, plan, ws = run_qk_prep(x, prep, w.grid, w.sparsity, tile=w.tile,
+                                     ref_keep=w.ref_keep, chunk_tiles=3)
+    assert plan.num_chunks > 1
+    q2, k2 = oracle_prep(x, prep)
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid, w.tile)
+    topk = oracle.topk_count(g.NV, w.sparsity)
+    H, D = w.heads, w.head_dim
+    inter = intermediates(plan, ws)
+    Nb = plan.num_blocks
+    qt = plan.view(ws, "qt", torch.int16, (H, Nb, 64, D)).cpu()
+    perm = g.perm().reshape(-1, 64)
+    got = out_f64(out)
+    sel_h = sel.cpu().numpy()
+    for h in range(H):
+        for name, x2, reg in (("Qt", q2, qt[h]), ("Kt", k2, inter["kt"][h])):
+            src = torch.from_numpy(np.ascontiguousarray(x2[:, h, :])).to(torch.bfloat16)
+            ref = torch.zeros((Nb, 64, D), dtype=torch.int16)
+            for b in range(Nb):
+                idx = perm[b][perm[b] >= 0]
+                ref[b, :len(idx)] = src.view(torch.int16)[torch.as_tensor(idx)]
+            assert torch.equal(reg, ref), f"{name} head {h}"
+        r = oracle.forward_head(q2, k2, x["v"], x["gate"], g, topk, h, ref_keep=w.ref_keep)
+        assert np.array_equal(inter["qp"][h], r.qp), f"pooled q head {h}"
+        assert np.array_equal(inter["kp"][h], r.kp), f"pooled k head {h}"
+        assert np.array_equal(sel_h[h], np.concatenate([r.ref_sel, r.sel], axis=1)), h
+        ref = (oracle.round_bf16_from_f64(r.out) if w.io_dtype == "bf16"
+               else r.out.astype(np.float32))
+        assert_close(got[:, h, :], ref, f"out head {h}")
+
+
+def test_wide_tiles_oneshot_equals_plan_forward():
+    """The one-call form with a 128-cell box builds the same plan and gives
+    the same output and selection, bit for bit."""
+    w = WORKLOADS["omniref_small"].with_(ref_keep=1.0)
+    x = make_inputs(w, seed=15)
+    out1, sel1, plan, _ = run(x, w.grid, w.sparsity, tile=w.tile)
+    xd = {n: x[n].cuda() for n in ("q", "k", "v", "gate")}
+    nbytes = vsa.vsa_h3_oneshot_workspace_bytes(x["token_tags"], x["position_ids"], w.grid,
+                                                w.tile, w.heads, w.head_dim, w.sparsity)
+    assert nbytes == plan.workspace_bytes
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out2 = torch.empty_like(xd["q"])
+    sel2 = torch.empty_like(sel1)
+    vsa.vsa_h3_forward_oneshot(xd["q"].data_ptr(), xd["k"].data_ptr(), xd["v"].data_ptr(),
+                               xd["gate"].data_ptr(), x["token_tags"].numpy(),
+                               x["position_ids"].numpy(), w.heads, w.head_dim, w.grid,
+                               w.sparsity, w.tile, vsa.VSA_BF16, out2.data_ptr(),
+                               sel2.data_ptr(), ws.data_ptr(), nbytes,
+                               torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(sel1, sel2)
 
 
 # ----------------------------------------------------------------- full-size OmniRef layout
