@@ -152,11 +152,11 @@ def sources_digest(paths):
     return h.hexdigest()
 
 
-def load_traffic(launches: int, workload: str):
+def load_traffic(launches: int, workload: str, chunk_tiles: int):
     """HBM bytes per fine-attention launch (the forward's fine-branch bytes over
     its key-chunk launches) from the committed counter summary, or None if it
-    is missing or was taken on a different workload, kernel source or launch
-    count."""
+    is missing or was taken on a different workload, kernel source or key-chunk
+    schedule."""
     try:
         with open(TRAFFIC_FILE.format(workload=workload)) as f:
             t = json.load(f)
@@ -166,7 +166,7 @@ def load_traffic(launches: int, workload: str):
         return None
     if t.get("kernel_sources_sha256") != sources_digest(FINE_SOURCES):
         return None
-    if t.get("launches_per_forward") != launches:
+    if t.get("launches_per_forward") != launches or t.get("key_chunk_tiles") != chunk_tiles:
         return None
     return t.get("bytes_per_launch")
 
@@ -215,6 +215,8 @@ def main():
                     help="a workload name from workloads.WORKLOADS, e.g. omniref768p10s "
                          "(128-token tiles, reference keep 0.1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-tiles", type=int, default=0,
+                    help="key tiles per fine-branch key chunk (0: the library's default)")
     ap.add_argument("--qk-fp8", action="store_true",
                     help="time the forward with per-token FP8 (E4M3) q and k in the fine branch")
     ap.add_argument("--qk-prep", action="store_true",
@@ -244,7 +246,8 @@ def main():
     torch.cuda.set_device(dev)
     xd = {n: x[n].to(dev) for n in ("q", "k", "v", "gate")}
     plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim, w.sparsity,
-                    w.tile, qk_prep=args.qk_prep, qk_fp8=args.qk_fp8, ref_keep=w.ref_keep)
+                    w.tile, chunk_tiles=args.chunk_tiles, qk_prep=args.qk_prep,
+                    qk_fp8=args.qk_fp8, ref_keep=w.ref_keep)
     stream = torch.cuda.current_stream(dev)
     ws = plan.workspace(dev, stream.cuda_stream)
     out = torch.empty_like(xd["q"])
@@ -351,7 +354,7 @@ def main():
             "bound": "mfma", "kernel": "fine_attn_kernel",
             "achieved": round(fine_tflops, 2), "peak": fine_peak, "unit": "TFLOP/s",
             "frac": round(fine_tflops / fine_peak, 4),
-            "traffic": load_traffic(launches, w.name),
+            "traffic": load_traffic(launches, w.name, plan.chunk_tiles),
             "launches_per_forward": launches,
             "key_chunk_tiles": plan.chunk_tiles,
             "algorithmic_flops_per_launch": alg_fine / launches,
