@@ -18,10 +18,11 @@
 //   - tiles hold 64 or 128 tokens and are handled as 64-slot blocks (a
 //     128-token tile is two consecutive blocks);
 //   - one workgroup of 2 waves per (head, query block), or with 128-token
-//     tiles and bf16 q/k one of 4 waves per (head, query tile), so that the
-//     tile's two query blocks share every K/V load; wave w owns query rows
-//     32w..32w+31, gathered straight from the packed [L][H][D] input through
-//     the slot table into MFMA operand registers;
+//     tiles one of 4 waves per (head, query tile), so that the tile's two
+//     query blocks share every K/V load (FP8 keys at head_dim 64 keep two-wave
+//     blocks); wave w owns query rows 32w..32w+31, gathered straight from the
+//     packed [L][H][D] input through the slot table into MFMA operand
+//     registers;
 //   - the visit list is ascending (prefix tiles 0..P-1, or the listed ones,
 //     then the selected video tiles) and visits each tile's blocks in order,
 //     stepping over a block without valid keys (the second block of a
@@ -30,7 +31,7 @@
 //   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
 //     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
 //     global->LDS loads (global_load_lds_dwordx4, no register staging).  A
-//     slot is refilled with the next tile's half as soon as both waves have
+//     slot is refilled with the next tile's half as soon as all waves have
 //     read it, so each load has about three quarters of an iteration to land
 //     (32 KB of LDS per workgroup: four two-wave or two four-wave
 //     workgroups per CU);
@@ -56,8 +57,8 @@
 //     heads, head by head: the 32 CUs of an XCD sweep the same head's K/V;
 //   - long key lists are cut into key chunks, one launch each: every query
 //     tile of a head visits its tiles of the current chunk at about the same
-//     time, so those reads mostly hit the L2 (and the Infinity Cache) instead
-//     of HBM.  Each wave's running state (O^T, running max, its lanes' row
+//     time, so many of those reads hit the L2 (and the Infinity Cache)
+//     instead of HBM.  Each wave's running state (O^T, running max, its lanes' row
 //     sums) is stored in fp32 at the end of a launch and loaded at the start
 //     of the next; visit order and arithmetic are those of a single launch,
 //     so the result is the same bit for bit.
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   //   K half:   [KROWB/64 groups][32 keys][64 B]: chunks 4G..4G+3 of a key
   //             row; logical chunk c sits at (c ^ swz64(key)) in its group;
   //   V^T half: [D rows][64 B] (the 32 keys of the half), the same swizzle.
-  // DMA load number x (0..2*KH_LOADS-1, or 0..2*VH_LOADS-1, over both waves;
+  // DMA load number x (0..NW*KH_LOADS-1, or 0..NW*VH_LOADS-1, over all waves;
   // 64 lanes x 16 B each)
   // fills LDS chunks 64x..64x+63: K rows 16(x % 2) + lane/4 of group x/2,
   // V^T rows 16x + lane/4.  The lane part of the source offset is the same
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   __builtin_amdgcn_s_waitcnt(kWaitVm);
 
   // Slot ring: each half tile is requested as soon as its slot has been read
-  // by both waves, about three quarters of an iteration before it is needed.
+  // by all waves, about three quarters of an iteration before it is needed.
   // Issue order, in iteration t: V^T half 1 of t, then K half 0, K half 1 and
   // V^T half 0 of t + 1; each wait below counts the loads issued after the
   // half it needs.
