@@ -121,6 +121,9 @@ typedef struct {
                        tile visits, ascending: the non-reference prefix tiles, the selected
                        reference tiles and the selected video tiles,
                        V = (num_prefix_tiles - num_ref_tiles) + topk_ref + topk */
+  uint64_t order;   /* int32 [H][num_chunks][Nt] (only if num_chunks > 1): the query tiles of
+                       each head in the order the fine branch dispatches them for each key
+                       chunk, most visits in the chunk first (ties in no fixed order) */
 } vsa_h3_ws_layout;
 
 /* Top-k rule of VSA-H3 evaluated in IEEE double as written; 0 when

@@ -102,3 +102,18 @@ def assert_close(got, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2):
 
 def out_f64(out: torch.Tensor) -> np.ndarray:
     return out.detach().to("cpu").to(torch.float64).numpy()
+
+
+def check_dispatch_order(plan, ws, offsets, pvis):
+    """offsets [H][NV][C+1]: listed tiles of each video query tile below each
+    chunk boundary; pvis: the implicit prefix tiles of the fine list."""
+    H, Nt, P, C = plan.heads, plan.num_tiles, plan.num_prefix_tiles, plan.num_chunks
+    order = plan.view(ws, "order", torch.int32, (H, C, Nt)).cpu().numpy()
+    for c in range(C):
+        lo, hi = c * plan.chunk_tiles, min((c + 1) * plan.chunk_tiles, Nt)
+        for h in range(H):
+            work = np.full(Nt, hi - lo)
+            work[P:] = (min(hi, pvis) - min(lo, pvis)) + offsets[h, :, c + 1] - offsets[h, :, c]
+            o = order[h, c]
+            assert np.array_equal(np.sort(o), np.arange(Nt)), (h, c)
+            assert np.all(np.diff(work[o]) <= 0), (h, c)

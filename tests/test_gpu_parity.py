@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import video_dit_block_amd as vsa
-from tests.gpu_helpers import (assert_close, errors, intermediates, out_f64, require_gpu, run,
-                               say)
+from tests.gpu_helpers import (assert_close, check_dispatch_order, errors, intermediates,
+                               out_f64, require_gpu, run, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +31,9 @@ def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
 
 
 def check_chunk_offsets(plan, ws, sel):
-    """Entry c of a row counts its selected tiles with id < c * chunk_tiles."""
+    """Entry c of a row counts its selected tiles with id < c * chunk_tiles;
+    the dispatch order of each (head, chunk) holds every query tile once,
+    sorted by its visits in the chunk, most first."""
     if plan.num_chunks <= 1 or plan.num_video_tiles == 0:
         return
     H, NV, C = plan.heads, plan.num_video_tiles, plan.num_chunks
@@ -40,6 +42,7 @@ def check_chunk_offsets(plan, ws, sel):
     s = sel.cpu().numpy()
     want = (s[:, :, :, None] < bounds[None, None, None, :]).sum(axis=2)
     assert np.array_equal(got, want)
+    check_dispatch_order(plan, ws, want, plan.num_prefix_tiles)
 
 
 def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True, plan=None):

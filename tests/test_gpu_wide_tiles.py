@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import video_dit_block_amd as vsa
-from tests.gpu_helpers import (assert_close, errors, intermediates, oracle_prep, out_f64,
-                               require_gpu, run, run_qk_prep, say)
+from tests.gpu_helpers import (assert_close, check_dispatch_order, errors, intermediates,
+                               oracle_prep, out_f64, require_gpu, run, run_qk_prep, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs, make_qk_prep_inputs
 
 pytestmark = pytest.mark.gpu
@@ -56,6 +56,8 @@ def _check_lists(plan, ws, g, lists_by_head):
         for h, lst in lists_by_head.items():
             want = (lst[:, :, None] < bounds[None, None, :]).sum(axis=1)
             assert np.array_equal(co[h], want), f"chunk offsets head {h}"
+        if len(lists_by_head) == H:
+            check_dispatch_order(plan, ws, co, 0 if plan.topk_ref > 0 else plan.num_prefix_tiles)
 
 
 def wide_check(w: Workload, x, plan=None, heads=None, check_tiles=True, qk_fp8=False,

@@ -57,7 +57,7 @@ class WsLayout(ctypes.Structure):
                [("scores_row_stride", ctypes.c_int64), ("chunk_offsets", ctypes.c_uint64),
                 ("state", ctypes.c_uint64), ("qt", ctypes.c_uint64), ("kt8", ctypes.c_uint64),
                 ("kscale", ctypes.c_uint64), ("kind", ctypes.c_uint64),
-                ("visit", ctypes.c_uint64)]
+                ("visit", ctypes.c_uint64), ("order", ctypes.c_uint64)]
 
 
 _lib = None

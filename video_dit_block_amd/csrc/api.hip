@@ -171,6 +171,7 @@ vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out) {
   out->kscale = lo.kscale;
   out->kind = lo.kind;
   out->visit = lo.visit;
+  out->order = lo.order;
   return VSA_OK;
 }
 
@@ -301,19 +302,21 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
 
   int32_t* visit = topk_ref > 0 ? reinterpret_cast<int32_t*>(ws + lo.visit) : nullptr;
   const int32_t* kind = reinterpret_cast<const int32_t*>(ws + lo.kind);
+  // With a reference selection every key tile of a video query comes from
+  // its visit list; otherwise the prefix tiles are implicit and sel follows.
+  const int pvis = topk_ref > 0 ? 0 : P;
+  int32_t* order = nchunks > 1 ? reinterpret_cast<int32_t*>(ws + lo.order) : nullptr;
   vsa::CoarseArgs ca{qp, kp, vp, scores, coarse, sel, choff, H, Nt, static_cast<int>(lo.ns),
-                     P, NV, topk, D, nchunks, chunk_tiles, kind, topk_ref, visit, visit_len};
+                     P, NV, topk, D, nchunks, chunk_tiles, kind, topk_ref, visit, visit_len,
+                     order, pvis};
   err = vsa::launch_coarse(ca, s);
   if (err != hipSuccess) return hip_fail("coarse launch", err);
   if ((err = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", err);
 
-  // With a reference selection every key tile of a video query comes from
-  // its visit list; otherwise the prefix tiles are implicit and sel follows.
   const int32_t* list = topk_ref > 0 ? visit : sel;
   const int listlen = topk_ref > 0 ? visit_len : topk;
-  const int pvis = topk_ref > 0 ? 0 : P;
   vsa::FineArgs fa{q, pp.qt, gate, out, f32, kt, vt, coarse, perm, valid, list, choff, state,
-                   H, Nt, P, NV, listlen, D, nchunks, chunk_tiles, kt8, kscale, bsh, pvis};
+                   H, Nt, P, NV, listlen, D, nchunks, chunk_tiles, kt8, kscale, bsh, pvis, order};
   err = vsa::launch_fine(fa, s);
   if (err != hipSuccess) return hip_fail("fine_attn launch", err);
   if ((err = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", err);

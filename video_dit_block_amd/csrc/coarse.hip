@@ -31,6 +31,7 @@ namespace vsa {
 namespace {
 
 constexpr int kScoreTile = 64;
+constexpr int kMaxTiles = 4096;   // tiles per head the plan accepts
 constexpr int kDChunk = 32;
 constexpr int kPad = 4;
 
@@ -230,6 +231,53 @@ __global__ __launch_bounds__(256) void coarse_softmax_topk_kernel(
   }
 }
 
+// Dispatch order of one head's query tiles in one key-chunk launch: the
+// tiles sorted by their visits in the chunk, most first, so that the long
+// blocks start first and the launch does not end on one of them (a counting
+// sort; the order among equal counts is whatever the LDS atomics give, which
+// changes no block's arithmetic).  One workgroup per (chunk, head).
+__global__ __launch_bounds__(1024) void chunk_order_kernel(const int32_t* __restrict__ choff,
+                                                           int Nt, int P, int NV, int nchunks,
+                                                           int chunk_tiles, int Pvis,
+                                                           int32_t* __restrict__ order) {
+  __shared__ int cnt[kMaxTiles + 2];
+  __shared__ int part[1024];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lo = c * chunk_tiles, hi = min(lo + chunk_tiles, Nt);
+  const int wmax = hi - lo;  // a prefix (dense) query tile visits every tile of the chunk
+  auto work = [&](int i) -> int {
+    if (i < P) return wmax;
+    const int32_t* co = choff + (static_cast<size_t>(h) * NV + (i - P)) * (nchunks + 1) + c;
+    return min(max(min(hi, Pvis) - min(lo, Pvis) + co[1] - co[0], 0), wmax);
+  };
+  for (int w = tid; w <= wmax; w += 1024) cnt[w] = 0;
+  __syncthreads();
+  for (int i = tid; i < Nt; i += 1024) atomicAdd(&cnt[wmax - work(i)], 1);
+  __syncthreads();
+  // Exclusive prefix sum of cnt over d = wmax - work (most work first):
+  // each thread sums a run of R entries, then the 1024 run sums are scanned.
+  const int R = (wmax + 1 + 1023) / 1024;
+  int run = 0;
+  for (int d = tid * R; d < min((tid + 1) * R, wmax + 1); ++d) run += cnt[d];
+  part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int base = part[tid] - run;
+  for (int d = tid * R; d < min((tid + 1) * R, wmax + 1); ++d) {
+    const int n = cnt[d];
+    cnt[d] = base;
+    base += n;
+  }
+  __syncthreads();
+  int32_t* dst = order + (static_cast<size_t>(h) * nchunks + c) * Nt;
+  for (int i = tid; i < Nt; i += 1024) dst[atomicAdd(&cnt[wmax - work(i)], 1)] = i;
+}
+
 // c[h] = Pr[h] @ vp[h]; block = 64 query tiles x D channels, K-loop over 32 key tiles.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict__ Pr,
@@ -351,6 +399,12 @@ hipError_t launch_d(const CoarseArgs& a, hipStream_t stream) {
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
+  if (a.order) {
+    hipLaunchKernelGGL(chunk_order_kernel, dim3(a.nchunks, a.H), dim3(1024), 0, stream, a.choff,
+                       a.Nt, a.P, a.NV, a.nchunks, a.chunk_tiles, a.Pvis, a.order);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL((coarse_pv_kernel<D>), dim3(nb, a.H), dim3(256), 0, stream, a.scores, a.vp,
                      a.Nt, a.Ns, a.coarse);
   return hipGetLastError();

@@ -237,10 +237,19 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   // 128-token tile with four.
   constexpr int ish = NW == 4 ? 1 : 0;
   int hd, ib;  // head, first query block of the item
-  if (a.nchunks > 1)
-    decode_item_chunked(blockIdx.x, H, Nb >> ish, hd, ib);
-  else
+  if (a.nchunks > 1) {
+    // The items of a head run in the chunk's order of its query tiles, the
+    // tiles with the most visits first (an item is a tile or one of its
+    // blocks).
+    int s;
+    decode_item_chunked(blockIdx.x, H, Nb >> ish, hd, s);
+    constexpr int sub = bsh - ish;
+    const int t = min(max(a.order[(static_cast<size_t>(hd) * a.nchunks + chunk) * Nt + (s >> sub)],
+                          0), Nt - 1);
+    ib = (t << sub) | (s & ((1 << sub) - 1));
+  } else {
     decode_item(blockIdx.x, H, (P << bsh) >> ish, (NV << bsh) >> ish, hd, ib);
+  }
   ib <<= ish;
   const int i = ib >> bsh;  // query tile
   const int nrows = NW == 4 ? valid[ib] + valid[ib + 1] : valid[ib];

@@ -48,6 +48,12 @@ struct CoarseArgs {
   int topk_ref;
   int32_t* visit;
   int visit_len;
+  // With nchunks > 1: order [H][nchunks][Nt] receives each head's query
+  // tiles sorted by their visits in the chunk, most first (the fine branch
+  // dispatches them in that order); the fine list holds tiles 0..Pvis-1
+  // implicitly.
+  int32_t* order;
+  int Pvis;
 };
 hipError_t launch_coarse(const CoarseArgs& a, hipStream_t stream);
 
@@ -73,6 +79,7 @@ struct FineArgs {
   const uint8_t* kt8;           // [H][Nb][64][D] E4M3 keys: FP8 Q/K logits, or null
   const float* kscale;          // [H][Nb][64]
   int bsh, Pvis;
+  const int32_t* order;         // [H][nchunks][Nt] dispatch order of query tiles (nchunks > 1)
 };
 hipError_t launch_fine(const FineArgs& a, hipStream_t stream);
 

@@ -73,6 +73,7 @@ void lay_out(vsa_h3_plan* plan) {
   lo.visit = take(plan->topk_ref > 0 ? h64 * nv64 * static_cast<uint64_t>(visit_len(plan)) * 4 : 0);
   const bool chunked = plan->num_chunks > 1;
   lo.choff = take(chunked ? h64 * nv64 * static_cast<uint64_t>(plan->num_chunks + 1) * 4 : 0);
+  lo.order = take(chunked ? h64 * static_cast<uint64_t>(plan->num_chunks) * nt64 * 4 : 0);
   // Two waves of 64 lanes per query block.
   lo.state = take(chunked ? h64 * nb64 * 2 * 64 *
                                 static_cast<uint64_t>(state_words_per_lane(plan->head_dim)) * 4

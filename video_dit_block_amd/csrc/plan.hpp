@@ -33,7 +33,7 @@ constexpr uint64_t kChunkBytesWide = uint64_t(32) << 20;
 
 struct Layout {
   uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, qt, kt8, kscale,
-      kind, visit, total;
+      kind, visit, order, total;
   int64_t ns;  // scores row stride
 };
 
