@@ -226,12 +226,13 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
     }
     // Vt: two halves of positions (0-31, 32-63), each [d][32] bf16 with
     // 16-byte chunks of 8 positions.  Positions p0..p0+7 (p0 = 8m) hold slots
-    // 16(m/2) + 4(m%2) + {0..3} and the same + 8.
+    // 16(m/2) + 4(m%2) + {0..3} and the same + 8.  Consecutive threads write
+    // consecutive 16-byte chunks (the four chunks of a row d, then row d+1).
     {
       uint16_t* dst = vt + tile_base * 64 * D;
       for (int c = tid; c < D * 8; c += blockDim.x) {
-        const int d = c % D;
-        const int m = c / D;
+        const int d = (c >> 2) % D;
+        const int m = 4 * ((c >> 2) / D) + (c & 3);
         const int sa = 16 * (m >> 1) + 4 * (m & 1);
         const int sb = sa + 8;
         uint4 o;
