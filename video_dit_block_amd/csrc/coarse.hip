@@ -278,82 +278,105 @@ __global__ __launch_bounds__(1024) void chunk_order_kernel(const int32_t* __rest
   for (int i = tid; i < Nt; i += 1024) dst[atomicAdd(&cnt[wmax - work(i)], 1)] = i;
 }
 
-// c[h] = Pr[h] @ vp[h]; block = 64 query tiles x D channels, K-loop over 32 key tiles.
+// c[h] = Pr[h] @ vp[h] on the fp32 matrix cores (v_mfma_f32_32x32x2_f32): a
+// block of 4 waves owns 64 query tiles x D channels, wave w the 32 rows
+// 32(w/2).. and the D/2 channels (D/2)(w%2)..; the K loop stages 32 key
+// tiles at a time in LDS (P transposed, [key][row], and vp, [key][channel]),
+// with row strides chosen so that the two lane halves of an operand read
+// (keys k and k+1) fall into (nearly) disjoint banks.  The order of the
+// fp32 sums is the matrix cores' own; c is compared with tolerance.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict__ Pr,
                                                         const float* __restrict__ vp, int Nt,
                                                         int Ns, float* __restrict__ c) {
-  constexpr int CPT = D / 16;   // channels per thread
   constexpr int KB = 32;
-  __shared__ __attribute__((aligned(16))) float ps[KB][64 + kPad];
-  __shared__ __attribute__((aligned(16))) float vs[KB][D];
+  constexpr int NTW = D / 64;          // 32x32 output tiles per wave
+  constexpr int PS = 64 + 33;          // 33 (mod 64): reads of keys k, k+1 and the
+  constexpr int VS = D + 32;           // transposing stores are at most 2-way conflicted
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  __shared__ __attribute__((aligned(16))) float ps[KB][PS];
+  __shared__ __attribute__((aligned(16))) float vs[KB][VS];
   const int h = blockIdx.y;
   const int i0 = blockIdx.x * 64;
   const int tid = threadIdx.x;
-  const int tr = tid / 16, tc = tid % 16;
+  const int w = tid >> 6, lane = tid & 63;
+  const int r0 = 32 * (w >> 1);
+  const int c0 = (D / 2) * (w & 1);
   const float* ph = Pr + static_cast<size_t>(h) * Nt * Ns;
   const float* vh = vp + static_cast<size_t>(h) * Nt * D;
-  float acc[4][CPT];
+  f32x16 acc[NTW];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < CPT; ++y) acc[x][y] = 0.0f;
+  for (int t = 0; t < NTW; ++t) acc[t] = f32x16{};
 
+  // The next 32 key tiles are loaded into registers while the matrix cores
+  // work on the current ones in LDS.
+  constexpr int NV4 = KB * D / 4 / 256;  // float4 of vp per thread
+  float4 pa[2], vb[NV4];
+  auto load = [&](int j0) {
+    // probabilities: 64 rows x 32 keys = 512 float4, 2 per thread
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int id = tid + e * 256;
+      const int r = id / 8, j = j0 + 4 * (id % 8);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i0 + r < Nt) {
+        const float* src = ph + static_cast<size_t>(i0 + r) * Ns + j;
+        if (j + 3 < Nt) {
+          x = *reinterpret_cast<const float4*>(src);
+        } else {
+          if (j + 0 < Nt) x.x = src[0];
+          if (j + 1 < Nt) x.y = src[1];
+          if (j + 2 < Nt) x.z = src[2];
+        }
+      }
+      pa[e] = x;
+    }
+    // pooled values: 32 rows x D (zero past the last key tile)
+#pragma unroll
+    for (int e = 0; e < NV4; ++e) {
+      const int id = tid + e * 256;
+      const int r = id / (D / 4), c4 = id % (D / 4);
+      vb[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + r < Nt) vb[e] = *reinterpret_cast<const float4*>(vh + static_cast<size_t>(j0 + r) * D + 4 * c4);
+    }
+  };
+  load(0);
   for (int j0 = 0; j0 < Nt; j0 += KB) {
-    // probabilities: 64 rows x 32 keys = 512 float4, 2 per thread (transposed into LDS)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int id = tid + e * 256;
       const int r = id / 8, c4 = id % 8;
-      const int j = j0 + 4 * c4;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i0 + r < Nt) {
-        const float* src = ph + static_cast<size_t>(i0 + r) * Ns + j;
-        if (j + 3 < Nt) {
-          a = *reinterpret_cast<const float4*>(src);
-        } else {
-          if (j + 0 < Nt) a.x = src[0];
-          if (j + 1 < Nt) a.y = src[1];
-          if (j + 2 < Nt) a.z = src[2];
-        }
-      }
-      ps[4 * c4 + 0][r] = a.x; ps[4 * c4 + 1][r] = a.y; ps[4 * c4 + 2][r] = a.z; ps[4 * c4 + 3][r] = a.w;
+      ps[4 * c4 + 0][r] = pa[e].x; ps[4 * c4 + 1][r] = pa[e].y;
+      ps[4 * c4 + 2][r] = pa[e].z; ps[4 * c4 + 3][r] = pa[e].w;
     }
-    // pooled values: 32 rows x D
-    for (int id = tid; id < KB * D / 4; id += 256) {
-      const int r = id / (D / 4), c4 = id % (D / 4);
-      float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j0 + r < Nt) b = *reinterpret_cast<const float4*>(vh + static_cast<size_t>(j0 + r) * D + 4 * c4);
-      *reinterpret_cast<float4*>(&vs[r][4 * c4]) = b;
+#pragma unroll
+    for (int e = 0; e < NV4; ++e) {
+      const int id = tid + e * 256;
+      *reinterpret_cast<float4*>(&vs[id / (D / 4)][4 * (id % (D / 4))]) = vb[e];
     }
     __syncthreads();
+    if (j0 + KB < Nt) load(j0 + KB);
+    // A: lane l holds P[row r0 + l%32][key k + l/32]; B: vp[key k + l/32][channel + l%32].
 #pragma unroll 4
-    for (int jj = 0; jj < KB; ++jj) {
-      const float4 a = *reinterpret_cast<const float4*>(&ps[jj][4 * tr]);
-      const float av[4] = {a.x, a.y, a.z, a.w};
-      float bv[CPT];
+    for (int k = 0; k < KB; k += 2) {
+      const float av = ps[k + (lane >> 5)][r0 + (lane & 31)];
 #pragma unroll
-      for (int y = 0; y < CPT; y += 4) {
-        const float4 b = *reinterpret_cast<const float4*>(&vs[jj][CPT * tc + y]);
-        bv[y] = b.x; bv[y + 1] = b.y; bv[y + 2] = b.z; bv[y + 3] = b.w;
+      for (int t = 0; t < NTW; ++t) {
+        const float bv = vs[k + (lane >> 5)][c0 + 32 * t + (lane & 31)];
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[t], 0, 0, 0);
       }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < CPT; ++y) acc[x][y] = fmaf(av[x], bv[y], acc[x][y]);
     }
     __syncthreads();
   }
+  // Accumulator register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32.
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int i = i0 + 4 * tr + x;
-    if (i < Nt) {
-      float* dst = c + (static_cast<size_t>(h) * Nt + i) * D + CPT * tc;
+  for (int t = 0; t < NTW; ++t)
 #pragma unroll
-      for (int y = 0; y < CPT; y += 4)
-        *reinterpret_cast<float4*>(dst + y) = make_float4(acc[x][y], acc[x][y + 1], acc[x][y + 2], acc[x][y + 3]);
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (i < Nt)
+        c[(static_cast<size_t>(h) * Nt + i) * D + c0 + 32 * t + (lane & 31)] = acc[t][r];
     }
-  }
 }
 
 template <int D>
