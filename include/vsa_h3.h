@@ -32,6 +32,11 @@
  *   - Device work is only enqueued on `stream` (a hipStream_t passed as
  *     void*; NULL is the null stream).  Calls do not synchronize, except that
  *     vsa_h3_plan_upload copies from pageable host memory.
+ *   - The forwards (vsa_h3_forward, vsa_h3_forward_qk_prep) enqueue kernel
+ *     launches only: no allocation, no memset, no copy, no host wait.  After
+ *     vsa_h3_plan_upload has filled a workspace they may be captured in a
+ *     HIP graph on `stream` and replayed; every workspace region other than
+ *     the uploaded tables is written before it is read within one forward.
  *   - Tensors are contiguous, sequence-major [L][heads][head_dim] (batch 1).
  *   - Indices are int32 on the device (L < 2^31); byte offsets are 64-bit.
  */
