@@ -530,8 +530,8 @@ def test_rope_scores_depend_only_on_position_difference():
         return oracle.qk_norm_rope(x, w, 0.0, np.cos(ang).astype(np.float32),
                                    np.sin(ang).astype(np.float32)).astype(np.float64)
     for p, pp in ((7, 3), (40, 2), (5, 5), (0, 11)):
-        lhs = float(rot(q, p) @ rot(k, pp).T)
-        rhs = float(rot(q, p - pp) @ rot(k, 0).T)
+        lhs = float((rot(q, p) @ rot(k, pp).T).item())
+        rhs = float((rot(q, p - pp) @ rot(k, 0).T).item())
         assert abs(lhs - rhs) < 2e-5 * D
 
 
