@@ -108,7 +108,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // many keys equal to T are still to be admitted.  Slots outside the group
 // hold key 0, which no candidate (>= 1) reaches: every real key is nonzero
 // (finite scores map above 2^23).  Counts are ballots and popcounts (scalar
-// unit), not lane sums.
+// unit), not lane sums.  The search fixes one bit of T per step, from the
+// top; once exactly k keys reach the candidate, T is the least of them, and
+// a wave minimum ends the search (typically half way for distinct scores).
 template <int MAXM>
 __device__ __forceinline__ void kth_key(const uint32_t (&key)[MAXM], int k, uint32_t& thr,
                                         int& need) {
@@ -118,7 +120,19 @@ __device__ __forceinline__ void kth_key(const uint32_t (&key)[MAXM], int k, uint
     int c = 0;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) c += __popcll(__builtin_amdgcn_ballot_w64(key[m] >= cand));
-    if (c >= k) thr = cand;
+    if (c >= k) {
+      thr = cand;
+      if (c == k) {   // wave-uniform
+        uint32_t mn = 0xffffffffu;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+          if (key[m] >= cand) mn = min(mn, key[m]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), o)));
+        thr = mn;
+        break;
+      }
+    }
   }
   int gt = 0;
 #pragma unroll
