@@ -129,6 +129,11 @@ typedef struct {
   uint64_t order;   /* int32 [H][num_chunks][Nt] (only if num_chunks > 1): the query tiles of
                        each head in the order the fine branch dispatches them for each key
                        chunk, most visits in the chunk first (ties in no fixed order) */
+  uint64_t kt_lo;   /* bf16, layout of kt (only for fp32 I/O, without FP8 keys): the low part
+                       bf16(x - bf16(x)) of every key element */
+  uint64_t vt_lo;   /* bf16, layout of vt (only for fp32 I/O): low parts of the values */
+  uint64_t qt_lo;   /* bf16, layout of qt (only for fp32 I/O with QK-norm + RoPE): low parts
+                       of the normalised, rotated queries */
 } vsa_h3_ws_layout;
 
 /* Top-k rule of VSA-H3 evaluated in IEEE double as written; 0 when
@@ -176,6 +181,18 @@ vsa_status vsa_h3_plan_info(const vsa_h3_plan* plan, vsa_h3_info* out);
 vsa_status vsa_h3_plan_set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles);
 vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out);
 
+/* I/O dtype the workspace is laid out for (VSA_BF16 by default).  A forward
+ * with io_dtype VSA_F32 needs a plan set to VSA_F32: its workspace also holds
+ * the low bf16 parts lo = bf16(x - bf16(x)) of the tile-ordered keys and
+ * values (and, with QK-norm + RoPE, queries).  The fine branch then forms
+ * every product of fp32 operands a, b as a_hi*b_hi + a_hi*b_lo + a_lo*b_hi on
+ * the bf16 matrix cores with fp32 sums, for q.k and for p.v alike, so its
+ * result carries fp32-level error (about 2^-16 relative per product) instead
+ * of bf16 rounding of the operands.  A VSA_F32 plan also runs bf16 forwards.
+ * The workspace size changes: call before sizing and uploading a workspace.
+ * VSA_E_ARG for another dtype. */
+vsa_status vsa_h3_plan_set_io_dtype(vsa_h3_plan* plan, vsa_dtype io_dtype);
+
 /* Host copies of the plan tables into caller-provided host buffers (any may
  * be NULL): perm int32 [Nt*tile_tokens], valid int32 [Nt] (tokens per tile),
  * tile_slot int32 [L] (tile*tile_tokens + slot of each packed token). */
@@ -201,8 +218,9 @@ vsa_status vsa_h3_plan_upload(const vsa_h3_plan* plan, void* workspace,
  *   workspace      device, 256-byte aligned, >= workspace_bytes, holding the
  *                  tables from vsa_h3_plan_upload.  Calls that overlap in
  *                  time must use different workspaces.
- * Errors: VSA_E_ARG for NULL buffers or an unknown dtype, VSA_E_WORKSPACE,
- * VSA_E_HIP if a launch fails (execution errors surface on the stream). */
+ * Errors: VSA_E_ARG for NULL buffers, an unknown dtype or VSA_F32 on a plan
+ * not set to it (vsa_h3_plan_set_io_dtype), VSA_E_WORKSPACE, VSA_E_HIP if a
+ * launch fails (execution errors surface on the stream). */
 vsa_status vsa_h3_forward(const vsa_h3_plan* plan, const void* q, const void* k, const void* v,
                           const void* gate, vsa_dtype io_dtype, void* out, int32_t* sel_idx,
                           void* workspace, uint64_t workspace_bytes, void* stream);
@@ -220,13 +238,13 @@ vsa_status vsa_h3_forward_timed(const vsa_h3_plan* plan, const void* q, const vo
                                 void* stream, void* const* events);
 
 /* One-call form: builds (or reuses from an internal, thread-safe cache) the
- * plan for these tags / positions / grid / sizes, uploads its tables into the
- * workspace and runs vsa_h3_forward.  Query the workspace size first with
- * vsa_h3_oneshot_workspace_bytes (same arguments). */
+ * plan for these tags / positions / grid / sizes / I/O dtype, uploads its
+ * tables into the workspace and runs vsa_h3_forward.  Query the workspace
+ * size first with vsa_h3_oneshot_workspace_bytes (same arguments). */
 vsa_status vsa_h3_oneshot_workspace_bytes(const int64_t* token_tags, const int64_t* position_ids,
                                           int64_t L, vsa_dims3 grid, vsa_dims3 tile,
                                           int32_t heads, int32_t head_dim, double sparsity,
-                                          uint64_t* bytes_out);
+                                          vsa_dtype io_dtype, uint64_t* bytes_out);
 vsa_status vsa_h3_forward_oneshot(const void* q, const void* k, const void* v, const void* gate,
                                   const int64_t* token_tags, const int64_t* position_ids,
                                   int64_t L, int32_t heads, int32_t head_dim, vsa_dims3 grid,

@@ -42,7 +42,7 @@ def test_forward_replays_from_a_captured_graph(name, w, opts):
     # Other inputs of the same shapes, for the eager forwards between replays.
     yd = {n: (xd[n].float() * -1.5 + 0.25).to(xd[n].dtype) for n in xd}
     plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim, w.sparsity,
-                    w.tile, ref_keep=w.ref_keep, **opts)
+                    w.tile, ref_keep=w.ref_keep, io_dtype=w.io_dtype, **opts)
     io = vsa.VSA_BF16 if w.io_dtype == "bf16" else vsa.VSA_F32
     prep = None
     if opts.get("qk_prep"):

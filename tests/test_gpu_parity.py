@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import video_dit_block_amd as vsa
-from tests.gpu_helpers import (assert_close, check_dispatch_order, errors, intermediates,
-                               out_f64, require_gpu, run, say)
+from tests.gpu_helpers import (F32_MAX_ABS, F32_REL_L2, assert_close, check_dispatch_order,
+                               errors, intermediates, out_f64, require_gpu, run, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -28,6 +28,12 @@ def _gpu():
 
 def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
     return x.to(torch.bfloat16).view(torch.int16)
+
+
+def _lo_bits(x: torch.Tensor) -> torch.Tensor:
+    """bf16 bits of x - bf16(x) (the low part of fp32 values)."""
+    x = x.to(torch.float32)
+    return (x - x.to(torch.bfloat16).to(torch.float32)).to(torch.bfloat16).view(torch.int16)
 
 
 def check_chunk_offsets(plan, ws, sel):
@@ -67,7 +73,10 @@ def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True, plan=None
         ma, rl = errors(inter["coarse"][h], r.c)
         assert ma < 1e-5 * max(1.0, float(np.abs(r.c).max())) + 1e-6, ("coarse", h, ma)
         ref = oracle.round_bf16_from_f64(r.out) if is_bf16 else r.out.astype(np.float32)
-        assert_close(got[:, h, :], ref, f"out head {h}")
+        if is_bf16:
+            assert_close(got[:, h, :], ref, f"out head {h}")
+        else:
+            assert_close(got[:, h, :], ref, f"out head {h} (fp32 bar)", F32_MAX_ABS, F32_REL_L2)
         if check_tiles:
             perm = g.perm()
             kt_ref = torch.zeros((g.Nt, 64, w.head_dim), dtype=torch.int16)
@@ -83,6 +92,21 @@ def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True, plan=None
             vt_cols = vt_ref.transpose(1, 2)[:, :, cols]
             vt_halves = vt_cols.reshape(g.Nt, w.head_dim, 2, 32).permute(0, 2, 1, 3)
             assert torch.equal(inter["vt"][h], vt_halves), f"V^T tiles head {h}"
+            if not is_bf16:
+                # low parts bf16(x - bf16(x)), same layouts
+                kl_ref = torch.zeros_like(kt_ref)
+                vl_ref = torch.zeros_like(vt_ref)
+                for j in range(g.Nt):
+                    idx = torch.as_tensor(perm[j][perm[j] >= 0])
+                    kl_ref[j, :len(idx)] = _lo_bits(x["k"][idx, h])
+                    vl_ref[j, :len(idx)] = _lo_bits(x["v"][idx, h])
+                Nb = plan.num_blocks
+                kt_lo = plan.view(ws, "kt_lo", torch.int16, (H, Nb, 64, w.head_dim))[h].cpu()
+                vt_lo = plan.view(ws, "vt_lo", torch.int16, (H, Nb, 2, w.head_dim, 32))[h].cpu()
+                assert torch.equal(kt_lo, kl_ref), f"K low parts head {h}"
+                vl_halves = vl_ref.transpose(1, 2)[:, :, cols].reshape(
+                    g.Nt, w.head_dim, 2, 32).permute(0, 2, 1, 3)
+                assert torch.equal(vt_lo, vl_halves), f"V^T low parts head {h}"
     return out, sel, plan, ws
 
 
@@ -143,11 +167,13 @@ def test_key_chunked_launches_match_oracle_and_single_launch(name, ch):
     w = Workload(name, H, D, io, prefix, grid, s)
     say(f"case {name}: chunk_tiles={ch}")
     x = make_inputs(w, seed=5, video_order=order)
-    plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, H, D, s, chunk_tiles=ch)
+    plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, H, D, s, chunk_tiles=ch,
+                    io_dtype=x["q"].dtype)
     nt = plan.num_tiles
     assert plan.num_chunks == -(-nt // min(ch, nt))
     out, sel, _, _ = full_check(w, x, s, plan=plan)
-    single = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, H, D, s, chunk_tiles=nt)
+    single = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, H, D, s, chunk_tiles=nt,
+                      io_dtype=x["q"].dtype)
     assert single.num_chunks == 1
     out1, sel1, _, _ = run(x, w.grid, s, plan=single)
     assert torch.equal(sel, sel1)
@@ -190,7 +216,7 @@ def test_repeatable_and_oneshot_identical():
     assert torch.equal(out1, out4) and torch.equal(sel1, sel4)
     xd = {n: x[n].cuda() for n in ("q", "k", "v", "gate")}
     nbytes = vsa.vsa_h3_oneshot_workspace_bytes(x["token_tags"], x["position_ids"], w.grid,
-                                                (4, 4, 4), 8, 128, w.sparsity)
+                                                (4, 4, 4), 8, 128, w.sparsity, vsa.VSA_BF16)
     ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out3 = torch.empty_like(xd["q"])
     sel3 = torch.empty_like(sel1)

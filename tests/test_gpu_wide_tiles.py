@@ -273,7 +273,8 @@ def test_wide_tiles_oneshot_equals_plan_forward():
     out1, sel1, plan, _ = run(x, w.grid, w.sparsity, tile=w.tile)
     xd = {n: x[n].cuda() for n in ("q", "k", "v", "gate")}
     nbytes = vsa.vsa_h3_oneshot_workspace_bytes(x["token_tags"], x["position_ids"], w.grid,
-                                                w.tile, w.heads, w.head_dim, w.sparsity)
+                                                w.tile, w.heads, w.head_dim, w.sparsity,
+                                                vsa.VSA_BF16)
     assert nbytes == plan.workspace_bytes
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out2 = torch.empty_like(xd["q"])

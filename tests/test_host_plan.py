@@ -312,3 +312,45 @@ def test_default_key_chunks_follow_the_key_format():
     vsa.vsa_h3_plan_set_qk_fp8(p.handle, False)
     info = vsa.vsa_h3_plan_info(p.handle)
     assert (info.chunk_tiles, info.num_chunks) == (319, 4)
+
+
+def test_fp32_io_plan_regions_and_errors():
+    """A plan laid out for fp32 I/O holds the low bf16 parts of the tile-ordered
+    keys and values (and of Qt with QK-norm + RoPE; no key low parts with FP8
+    keys); an fp32 forward on a bf16 plan is refused before any device work."""
+    w = WORKLOADS["tiny"]
+    tags, pos = make_layout(w)
+    p = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+    base = p.workspace_bytes
+    H, Nb, D = w.heads, p.num_blocks, w.head_dim
+    tok = H * Nb * 64 * D * 2
+    L = _abi.lib()
+    fake = 1 << 40   # never dereferenced: the call fails its checks first
+    ins = [fake, fake + (1 << 30), fake + (2 << 30), fake + (3 << 30)]
+    assert L.vsa_h3_forward(p.handle, *ins, _abi.VSA_F32, fake + (4 << 30), None,
+                            fake + (5 << 30), base, None) == _abi.VSA_E_ARG
+    assert "vsa_h3_plan_set_io_dtype" in vsa.vsa_h3_last_error()
+    f = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity, io_dtype="f32")
+    lo = f.layout
+    assert f.workspace_bytes >= base + 2 * tok
+    for off in (lo.kt_lo, lo.vt_lo):
+        assert off % 256 == 0 and off + tok <= lo.total
+    assert p.layout.kt_lo == p.layout.vt_lo == p.layout.qt_lo  # empty regions in a bf16 plan
+    fp = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity, qk_prep=True,
+                  io_dtype="f32")
+    assert fp.layout.qt_lo % 256 == 0 and fp.layout.qt_lo + tok <= fp.layout.total
+    f8 = vsa.Plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity, qk_fp8=True,
+                  io_dtype="f32")
+    assert f8.layout.vt_lo + tok <= f8.layout.total
+    assert f8.workspace_bytes < f8.layout.vt_lo + 2 * tok   # no key low parts with FP8 keys
+    # back to bf16: the low-part regions go
+    vsa.vsa_h3_plan_set_io_dtype(f.handle, vsa.VSA_BF16)
+    assert vsa.vsa_h3_plan_info(f.handle).workspace_bytes == base
+    assert L.vsa_h3_plan_set_io_dtype(f.handle, 7) == _abi.VSA_E_ARG
+    # the one-call form sizes its workspace by the I/O dtype
+    n16 = vsa.vsa_h3_oneshot_workspace_bytes(tags.numpy(), pos.numpy(), w.grid, (4, 4, 4), H, D,
+                                             w.sparsity, vsa.VSA_BF16)
+    n32 = vsa.vsa_h3_oneshot_workspace_bytes(tags.numpy(), pos.numpy(), w.grid, (4, 4, 4), H, D,
+                                             w.sparsity, vsa.VSA_F32)
+    assert (n16, n32) == (base, vsa.Plan(tags, pos, w.grid, H, D, w.sparsity,
+                                         io_dtype="f32").workspace_bytes)

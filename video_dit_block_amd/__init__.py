@@ -29,11 +29,25 @@ from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
     vsa_h3_oneshot_workspace_bytes, vsa_h3_plan_create, vsa_h3_plan_destroy, vsa_h3_plan_info,
     vsa_h3_plan_layout, vsa_h3_plan_set_chunk_tiles, vsa_h3_plan_tables, vsa_h3_plan_upload,
     vsa_h3_topk, vsa_h3_version, vsa_h3_plan_set_qk_prep, vsa_h3_forward_qk_prep,
-    vsa_h3_plan_set_qk_fp8, vsa_h3_plan_set_ref_keep,
+    vsa_h3_plan_set_qk_fp8, vsa_h3_plan_set_ref_keep, vsa_h3_plan_set_io_dtype,
 )
 
 __all__ = ["Plan", "forward", "forward_qk_prep", "VsaError", "vsa_h3_topk",
-           "vsa_h3_version"] + list(EXPORTED)
+           "vsa_h3_version", "io_dtype_code"] + list(EXPORTED)
+
+
+def io_dtype_code(dtype) -> int:
+    """VSA_BF16 or VSA_F32 for a torch dtype, "bf16" / "f32", or the code itself."""
+    if isinstance(dtype, int):
+        if dtype not in (VSA_BF16, VSA_F32):
+            raise VsaError(-1, f"unknown io dtype code {dtype}")
+        return dtype
+    name = str(dtype).replace("torch.", "")
+    if name in ("bf16", "bfloat16"):
+        return VSA_BF16
+    if name in ("f32", "fp32", "float32", "float"):
+        return VSA_F32
+    raise VsaError(-1, f"unsupported io dtype {dtype}")
 
 
 def _host_i64(x) -> np.ndarray:
@@ -51,7 +65,7 @@ class Plan:
 
     def __init__(self, token_tags, position_ids, grid, heads, head_dim, sparsity,
                  tile=(4, 4, 4), chunk_tiles: int = 0, qk_prep: bool = False,
-                 qk_fp8: bool = False, ref_keep: float = 1.0):
+                 qk_fp8: bool = False, ref_keep: float = 1.0, io_dtype="bf16"):
         self.token_tags = _host_i64(token_tags).reshape(-1)
         self.position_ids = _host_i64(position_ids).reshape(-1, 3)
         self.grid = tuple(int(g) for g in grid)
@@ -70,6 +84,10 @@ class Plan:
         if ref_keep != 1.0:
             vsa_h3_plan_set_ref_keep(self.handle, ref_keep)
         self.ref_keep = float(ref_keep)
+        # fp32 I/O needs the low-part regions of the workspace.
+        self.io_dtype = io_dtype_code(io_dtype)
+        if self.io_dtype == VSA_F32:
+            vsa_h3_plan_set_io_dtype(self.handle, VSA_F32)
         self.info = vsa_h3_plan_info(self.handle)
         self.layout = vsa_h3_plan_layout(self.handle)
         self._ws = {}
@@ -150,20 +168,21 @@ _plans_lock = threading.Lock()
 
 
 def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4, 4, 4),
-             qk_prep: bool = False, ref_keep: float = 1.0) -> Plan:
+             qk_prep: bool = False, ref_keep: float = 1.0, io_dtype="bf16") -> Plan:
     """Cached Plan for this exact layout (keyed by a digest of tags and positions)."""
     tags = _host_i64(token_tags).reshape(-1)
     pos = _host_i64(position_ids).reshape(-1, 3)
     digest = hashlib.sha256(tags.tobytes() + b"|" + pos.tobytes()).hexdigest()
+    io = io_dtype_code(io_dtype)
     key = (digest, tuple(grid), tuple(tile), int(heads), int(head_dim), float(sparsity),
-           bool(qk_prep), float(ref_keep))
+           bool(qk_prep), float(ref_keep), io)
     with _plans_lock:
         p = _plans.get(key)
         if p is not None:
             _plans.move_to_end(key)
             return p
     p = Plan(tags, pos, grid, heads, head_dim, sparsity, tile, qk_prep=qk_prep,
-             ref_keep=ref_keep)
+             ref_keep=ref_keep, io_dtype=io)
     with _plans_lock:
         _plans[key] = p
         while len(_plans) > 8:
@@ -197,9 +216,12 @@ def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsi
             raise VsaError(-1, "tensors must be contiguous")
     L, H, D = q.shape
     if plan is None:
-        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile, ref_keep=ref_keep)
+        plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile, ref_keep=ref_keep,
+                        io_dtype=io)
     if (plan.L, plan.heads, plan.head_dim) != (L, H, D):
         raise VsaError(-1, "plan does not match the tensors' [L, heads, head_dim]")
+    if io == VSA_F32 and plan.io_dtype != VSA_F32:
+        raise VsaError(-1, "float32 tensors need a plan built with io_dtype='f32'")
     dev = q.device
     stream = torch.cuda.current_stream(dev).cuda_stream
     ws = plan.workspace(dev, stream)
@@ -245,9 +267,11 @@ def forward_qk_prep(q, k, v, gate, q_norm_weight, k_norm_weight, eps, rope_cos, 
             raise VsaError(-1, "tensors must be contiguous")
     if plan is None:
         plan = get_plan(token_tags, position_ids, grid, H, D, sparsity, tile, qk_prep=True,
-                        ref_keep=ref_keep)
+                        ref_keep=ref_keep, io_dtype=io)
     if not plan.qk_prep:
         raise VsaError(-1, "plan was built without qk_prep=True")
+    if io == VSA_F32 and plan.io_dtype != VSA_F32:
+        raise VsaError(-1, "float32 tensors need a plan built with io_dtype='f32'")
     if (plan.L, plan.heads, plan.head_dim) != (L, H, D):
         raise VsaError(-1, "plan does not match the tensors' [L, heads, head_dim]")
     dev = q.device

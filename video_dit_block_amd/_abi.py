@@ -26,7 +26,7 @@ EXPORTED = (
     "vsa_h3_plan_tables", "vsa_h3_plan_upload", "vsa_h3_forward", "vsa_h3_forward_timed",
     "vsa_h3_oneshot_workspace_bytes", "vsa_h3_forward_oneshot", "vsa_h3_plan_destroy",
     "vsa_h3_last_error", "vsa_h3_version", "vsa_h3_plan_set_qk_prep", "vsa_h3_forward_qk_prep",
-    "vsa_h3_plan_set_qk_fp8", "vsa_h3_plan_set_ref_keep",
+    "vsa_h3_plan_set_qk_fp8", "vsa_h3_plan_set_ref_keep", "vsa_h3_plan_set_io_dtype",
 )
 
 
@@ -57,7 +57,9 @@ class WsLayout(ctypes.Structure):
                [("scores_row_stride", ctypes.c_int64), ("chunk_offsets", ctypes.c_uint64),
                 ("state", ctypes.c_uint64), ("qt", ctypes.c_uint64), ("kt8", ctypes.c_uint64),
                 ("kscale", ctypes.c_uint64), ("kind", ctypes.c_uint64),
-                ("visit", ctypes.c_uint64), ("order", ctypes.c_uint64)]
+                ("visit", ctypes.c_uint64), ("order", ctypes.c_uint64),
+                ("kt_lo", ctypes.c_uint64), ("vt_lo", ctypes.c_uint64),
+                ("qt_lo", ctypes.c_uint64)]
 
 
 _lib = None
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_uint64, _P, ctypes.POINTER(_P)]
         L.vsa_h3_oneshot_workspace_bytes.argtypes = [_I64P, _I64P, ctypes.c_int64, Dims3, Dims3,
                                                      ctypes.c_int32, ctypes.c_int32,
-                                                     ctypes.c_double,
+                                                     ctypes.c_double, ctypes.c_int,
                                                      ctypes.POINTER(ctypes.c_uint64)]
         L.vsa_h3_forward_oneshot.argtypes = [_P, _P, _P, _P, _I64P, _I64P, ctypes.c_int64,
                                              ctypes.c_int32, ctypes.c_int32, Dims3,
@@ -104,6 +106,7 @@ def lib() -> ctypes.CDLL:
         L.vsa_h3_plan_set_qk_prep.argtypes = [_P, ctypes.c_int32]
         L.vsa_h3_plan_set_qk_fp8.argtypes = [_P, ctypes.c_int32]
         L.vsa_h3_plan_set_ref_keep.argtypes = [_P, ctypes.c_double]
+        L.vsa_h3_plan_set_io_dtype.argtypes = [_P, ctypes.c_int]
         L.vsa_h3_forward_qk_prep.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                              ctypes.c_int, _P, _P, _P, ctypes.c_uint64, _P,
                                              ctypes.POINTER(_P)]
@@ -209,6 +212,10 @@ def vsa_h3_plan_set_ref_keep(plan: int, keep: float) -> None:
     check(lib().vsa_h3_plan_set_ref_keep(plan, float(keep)))
 
 
+def vsa_h3_plan_set_io_dtype(plan: int, io_dtype: int) -> None:
+    check(lib().vsa_h3_plan_set_io_dtype(plan, int(io_dtype)))
+
+
 def vsa_h3_forward_qk_prep(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr: int,
                            q_norm_weight_ptr: int, k_norm_weight_ptr: int, eps: float,
                            rope_cos_ptr: int, rope_sin_ptr: int, io_dtype: int, out_ptr: int,
@@ -222,13 +229,14 @@ def vsa_h3_forward_qk_prep(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_p
 
 
 def vsa_h3_oneshot_workspace_bytes(token_tags, position_ids, grid, tile, heads, head_dim,
-                                   sparsity) -> int:
+                                   sparsity, io_dtype: int = VSA_BF16) -> int:
     tags = _i64(token_tags).reshape(-1)
     pos = _i64(position_ids).reshape(-1, 3)
     n = ctypes.c_uint64()
     check(lib().vsa_h3_oneshot_workspace_bytes(_ptr64(tags), _ptr64(pos), tags.shape[0],
                                                Dims3(*grid), Dims3(*tile), int(heads),
-                                               int(head_dim), float(sparsity), ctypes.byref(n)))
+                                               int(head_dim), float(sparsity), int(io_dtype),
+                                               ctypes.byref(n)))
     return n.value
 
 

@@ -47,6 +47,7 @@ struct CacheEntry {
   vsa_dims3 grid, tile;
   int32_t heads, head_dim;
   double sparsity;
+  bool io_f32;
   std::shared_ptr<const vsa_h3_plan> plan;
 };
 std::mutex g_cache_mu;
@@ -55,14 +56,20 @@ constexpr size_t kCacheMax = 8;
 
 vsa_status cached_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_dims3 grid,
                        vsa_dims3 tile, int32_t heads, int32_t head_dim, double sparsity,
-                       std::shared_ptr<const vsa_h3_plan>* out) {
+                       vsa_dtype io_dtype, std::shared_ptr<const vsa_h3_plan>* out) {
   if (L < 0 || (L > 0 && (!tags || !pos))) {
     set_error("token_tags / position_ids must be non-NULL for L > 0");
     return VSA_E_ARG;
   }
+  if (io_dtype != VSA_BF16 && io_dtype != VSA_F32) {
+    set_error("io_dtype must be VSA_BF16 or VSA_F32");
+    return VSA_E_ARG;
+  }
+  const bool f32 = io_dtype == VSA_F32;
   std::lock_guard<std::mutex> lock(g_cache_mu);
   for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
     if (it->heads == heads && it->head_dim == head_dim && it->sparsity == sparsity &&
+        it->io_f32 == f32 &&
         it->grid.t == grid.t && it->grid.h == grid.h && it->grid.w == grid.w &&
         it->tile.t == tile.t && it->tile.h == tile.h && it->tile.w == tile.w &&
         static_cast<int64_t>(it->tags.size()) == L &&
@@ -76,6 +83,7 @@ vsa_status cached_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_d
   auto plan = std::make_shared<vsa_h3_plan>();
   vsa_status st = vsa::build_plan(tags, pos, L, grid, tile, heads, head_dim, sparsity, plan.get());
   if (st != VSA_OK) return st;
+  if (f32) vsa::set_io_f32(plan.get(), true);
   CacheEntry e;
   e.tags.assign(tags, tags + L);
   e.pos.assign(pos, pos + 3 * L);
@@ -84,6 +92,7 @@ vsa_status cached_plan(const int64_t* tags, const int64_t* pos, int64_t L, vsa_d
   e.heads = heads;
   e.head_dim = head_dim;
   e.sparsity = sparsity;
+  e.io_f32 = f32;
   e.plan = std::move(plan);
   g_cache.push_front(std::move(e));
   if (g_cache.size() > kCacheMax) g_cache.pop_back();
@@ -172,6 +181,22 @@ vsa_status vsa_h3_plan_layout(const vsa_h3_plan* plan, vsa_h3_ws_layout* out) {
   out->kind = lo.kind;
   out->visit = lo.visit;
   out->order = lo.order;
+  out->kt_lo = lo.kt_lo;
+  out->vt_lo = lo.vt_lo;
+  out->qt_lo = lo.qt_lo;
+  return VSA_OK;
+}
+
+vsa_status vsa_h3_plan_set_io_dtype(vsa_h3_plan* plan, vsa_dtype io_dtype) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return VSA_E_ARG;
+  }
+  if (io_dtype != VSA_BF16 && io_dtype != VSA_F32) {
+    set_error("io_dtype must be VSA_BF16 or VSA_F32");
+    return VSA_E_ARG;
+  }
+  vsa::set_io_f32(plan, io_dtype == VSA_F32);
   return VSA_OK;
 }
 
@@ -235,6 +260,11 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
     set_error("io_dtype must be VSA_BF16 or VSA_F32");
     return VSA_E_ARG;
   }
+  if (io_dtype == VSA_F32 && !plan->io_f32) {
+    set_error("fp32 I/O needs a plan laid out for it: call vsa_h3_plan_set_io_dtype(plan, "
+              "VSA_F32) before sizing the workspace");
+    return VSA_E_ARG;
+  }
   vsa_status st = check_workspace(plan, workspace, workspace_bytes);
   if (st != VSA_OK) return st;
   if (plan->L == 0) return VSA_OK;
@@ -287,15 +317,19 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
   };
   hipError_t err = mark(0);
   if (err != hipSuccess) return hip_fail("hipEventRecord", err);
+  // fp32 I/O: the low bf16 parts of the tile-ordered operands.
+  uint16_t* kt_lo = f32 && !plan->qk_fp8 ? reinterpret_cast<uint16_t*>(ws + lo.kt_lo) : nullptr;
+  uint16_t* vt_lo = f32 ? reinterpret_cast<uint16_t*>(ws + lo.vt_lo) : nullptr;
   vsa::QkPrepArgs pp{};
   if (prep) {
     pp = *prep;
     pp.qt = reinterpret_cast<uint16_t*>(ws + lo.qt);
+    pp.qt_lo = f32 ? reinterpret_cast<uint16_t*>(ws + lo.qt_lo) : nullptr;
   }
   uint8_t* kt8 = plan->qk_fp8 ? reinterpret_cast<uint8_t*>(ws + lo.kt8) : nullptr;
   float* kscale = plan->qk_fp8 ? reinterpret_cast<float*>(ws + lo.kscale) : nullptr;
   vsa::PermutePoolArgs pa{q, k, v, f32, perm, valid, H, Nt, D, bsh, kt, vt, qp, kp, vp, pp, kt8,
-                          kscale};
+                          kscale, kt_lo, vt_lo};
   err = vsa::launch_permute_pool(pa, s);
   if (err != hipSuccess) return hip_fail("permute_pool launch", err);
   if ((err = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", err);
@@ -316,7 +350,8 @@ vsa_status run_forward(const vsa_h3_plan* plan, const void* q, const void* k, co
   const int32_t* list = topk_ref > 0 ? visit : sel;
   const int listlen = topk_ref > 0 ? visit_len : topk;
   vsa::FineArgs fa{q, pp.qt, gate, out, f32, kt, vt, coarse, perm, valid, list, choff, state,
-                   H, Nt, P, NV, listlen, D, nchunks, chunk_tiles, kt8, kscale, bsh, pvis, order};
+                   H, Nt, P, NV, listlen, D, nchunks, chunk_tiles, kt8, kscale, bsh, pvis, order,
+                   kt_lo, vt_lo, pp.qt_lo};
   err = vsa::launch_fine(fa, s);
   if (err != hipSuccess) return hip_fail("fine_attn launch", err);
   if ((err = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", err);
@@ -391,7 +426,7 @@ vsa_status vsa_h3_forward_qk_prep(const vsa_h3_plan* plan, const void* q, const 
       return VSA_E_ARG;
     }
   }
-  vsa::QkPrepArgs prep{q_norm_weight, k_norm_weight, rope_cos, rope_sin, eps, nullptr};
+  vsa::QkPrepArgs prep{q_norm_weight, k_norm_weight, rope_cos, rope_sin, eps, nullptr, nullptr};
   return run_forward(plan, q, k, v, gate, &prep, io_dtype, out, sel_idx, workspace,
                      workspace_bytes, stream, events);
 }
@@ -399,14 +434,14 @@ vsa_status vsa_h3_forward_qk_prep(const vsa_h3_plan* plan, const void* q, const 
 vsa_status vsa_h3_oneshot_workspace_bytes(const int64_t* token_tags, const int64_t* position_ids,
                                           int64_t L, vsa_dims3 grid, vsa_dims3 tile,
                                           int32_t heads, int32_t head_dim, double sparsity,
-                                          uint64_t* bytes_out) {
+                                          vsa_dtype io_dtype, uint64_t* bytes_out) {
   if (!bytes_out) {
     set_error("bytes_out is NULL");
     return VSA_E_ARG;
   }
   std::shared_ptr<const vsa_h3_plan> plan;
   vsa_status st = cached_plan(token_tags, position_ids, L, grid, tile, heads, head_dim, sparsity,
-                              &plan);
+                              io_dtype, &plan);
   if (st != VSA_OK) return st;
   *bytes_out = plan->layout.total;
   return VSA_OK;
@@ -420,7 +455,7 @@ vsa_status vsa_h3_forward_oneshot(const void* q, const void* k, const void* v, c
                                   void* stream) {
   std::shared_ptr<const vsa_h3_plan> plan;
   vsa_status st = cached_plan(token_tags, position_ids, L, grid, tile, heads, head_dim, sparsity,
-                              &plan);
+                              io_dtype, &plan);
   if (st != VSA_OK) return st;
   st = vsa_h3_plan_upload(plan.get(), workspace, workspace_bytes, stream);
   if (st != VSA_OK) return st;

@@ -33,6 +33,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// Low parts of a two-term bf16 split of two fp32 values: bf16(x - bf16(x))
+// (the subtraction is exact), packed like pack_bf16x2.  hi + lo represents x
+// to about 2^-17 relative.
+__device__ __forceinline__ uint32_t pack_bf16x2_lo(float lo, float hi) {
+  const uint32_t h = pack_bf16x2(lo, hi);
+  return pack_bf16x2(lo - __uint_as_float(h << 16), hi - __uint_as_float(h & 0xffff0000u));
+}
+
 // Input element -> fp32 (exact for both supported I/O types).
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }

@@ -55,6 +55,12 @@
 //     when it has to rise;
 //   - blocks are mapped to the 8 XCDs so that each XCD works through its own
 //     heads, head by head: the 32 CUs of an XCD sweep the same head's K/V;
+//   - fp32 I/O keeps fp32-level accuracy on the bf16 matrix cores: every
+//     operand x is split into bf16 parts hi = bf16(x), lo = bf16(x - hi), and
+//     each product a*b is formed as a_hi*b_hi + a_hi*b_lo + a_lo*b_hi with
+//     fp32 sums (three MFMAs per step of Q.K and of P.V; the dropped a_lo*b_lo
+//     and the split residues are about 2^-16 of |a*b|); K and V^T arrive with
+//     their low parts in the same slot, so the LDS ring doubles;
 //   - long key lists are cut into key chunks, one launch each: every query
 //     tile of a head visits its tiles of the current chunk at about the same
 //     time, so many of those reads hit the L2 (and the Infinity Cache)
@@ -99,7 +105,7 @@ struct IoOps<uint16_t> {  // bf16 I/O
 };
 
 template <>
-struct IoOps<float> {  // fp32 I/O; the MFMA operands are rounded to bf16
+struct IoOps<float> {  // fp32 I/O; load8 gives the high bf16 parts, load8_lo the low parts
   static __device__ __forceinline__ bf16x8 load8(const float* p) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -108,6 +114,16 @@ struct IoOps<float> {  // fp32 I/O; the MFMA operands are rounded to bf16
     u.y = pack_bf16x2(a.z, a.w);
     u.z = pack_bf16x2(b.x, b.y);
     u.w = pack_bf16x2(b.z, b.w);
+    return __builtin_bit_cast(bf16x8, u);
+  }
+  static __device__ __forceinline__ bf16x8 load8_lo(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    u32x4 u;
+    u.x = pack_bf16x2_lo(a.x, a.y);
+    u.y = pack_bf16x2_lo(a.z, a.w);
+    u.z = pack_bf16x2_lo(b.x, b.y);
+    u.w = pack_bf16x2_lo(b.z, b.w);
     return __builtin_bit_cast(bf16x8, u);
   }
   static __device__ __forceinline__ void load4(const float* p, float v[4]) {
@@ -171,6 +187,8 @@ __device__ __forceinline__ void decode_item_chunked(int b, int H, int n, int& h,
 // by the compiler's own wait-count pass, which then does not add a
 // conservative vmcnt(0) in front of the LDS reads.
 constexpr int kWaitVm = 0x0F70;
+// The same with vmcnt <= N for N < 64 (vmcnt bits 5:4 sit in bits 15:14).
+constexpr int wait_vm_imm(int n) { return kWaitVm | (n & 15) | ((n >> 4) << 14); }
 
 // XOR swizzle of the 16-byte chunk index inside a 64-byte LDS row: rows
 // r, r + 4, r + 8, r + 12 differ, so the 16 lanes of one pass of a 16-byte
@@ -184,6 +202,11 @@ __device__ __forceinline__ float pinned(float x) {
   return x;
 }
 
+// High and low bf16 parts of eight operand values (fp32 I/O).
+struct Bf16Pair {
+  bf16x8 h, l;
+};
+
 // Eight input values as fp32.
 template <typename TIO>
 __device__ __forceinline__ void load_f32x8(const TIO* p, float v[8]) {
@@ -194,8 +217,13 @@ __device__ __forceinline__ void load_f32x8(const TIO* p, float v[8]) {
 // NW waves per block own NW * 32 query rows: 2 (a 64-slot block) or 4 (a
 // whole 128-token tile, whose two blocks share every K/V load).  A tile is
 // 1 << BSH blocks (BSH 0: 64-token tiles, 1: 128-token tiles).
+// fp32 I/O (TIO float) carries low parts of every operand: more registers,
+// so one wave per SIMD is allowed there.
+template <typename TIO>
+constexpr int kFineMinWaves = sizeof(TIO) == 4 ? 1 : 2;
+
 template <typename TIO, int D, bool QK8, int NW, int BSH>
-__global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
+__global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(FineArgs a,
                                                           const int32_t* __restrict__ valid,
                                                           const int32_t* __restrict__ list,
                                                           const int32_t* __restrict__ choff,
@@ -211,17 +239,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   constexpr int VH_LOADS = VH_BYTES / 1024 / NW;  // the same per V^T half
   static_assert(KH_LOADS * NW * 1024 == KH_BYTES && VH_LOADS * NW * 1024 == VH_BYTES,
                 "a half splits evenly over the waves");
+  // fp32 I/O: K (unless FP8) and V^T come with low bf16 parts, stored right
+  // after the high parts in each slot.
+  constexpr bool SPLIT = std::is_same<TIO, float>::value;
+  constexpr bool KSPLIT = SPLIT && !QK8;
+  constexpr int KPARTS = KSPLIT ? 2 : 1;
+  constexpr int VPARTS = SPLIT ? 2 : 1;
   constexpr int NK64 = D / 64;                   // FP8 MFMA steps of 64 channels
   constexpr int NCK = D / 16;                    // QK contraction steps
   constexpr int NB = D / 32;                     // O^T blocks of 32 channels
   // Four LDS slots, one per half tile: K keys 0-31, K keys 32-63, V^T keys
   // 0-31 and V^T keys 32-63.  With QK8 a K slot is followed by 1 KB per wave
   // for per-key scales (the first 64 bytes hold the wave's 16 scales).
-  constexpr int KSLOT = QK8 ? KH_BYTES + 2048 : KH_BYTES;
+  constexpr int KSLOT = QK8 ? KH_BYTES + 2048 : KPARTS * KH_BYTES;
+  constexpr int VSLOT = VPARTS * VH_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds_ka[KSLOT];
   __shared__ __attribute__((aligned(1024))) char lds_kb[KSLOT];
-  __shared__ __attribute__((aligned(1024))) char lds_va[VH_BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_vb[VH_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_va[VSLOT];
+  __shared__ __attribute__((aligned(1024))) char lds_vb[VSLOT];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -290,6 +325,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   // Rows come from the packed input, or from the tile-ordered copy that the
   // gather wrote after QK-norm and RoPE (pad rows are zero there).
   bf16x8 qf[QK8 ? 1 : NCK];
+  bf16x8 qfl[KSPLIT ? NCK : 1];   // fp32 I/O: low parts
   // QK8: this lane's 64 channels 64m + 32hl + 0..31 (m < NK64) of its query
   // row as E4M3 codes of x * (448 / amax) (amax over the whole row), and the
   // row's dequantisation scale amax / 448 (zero rows: zero codes and scale).
@@ -303,8 +339,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
       for (int g = 0; g < 4; ++g) {
         const int d0 = 64 * m + 32 * hl + 8 * g;
         if (a.qt) {
-          load_f32x8(a.qt + ((static_cast<size_t>(hd) * Nb + ib) * 64 + 32 * w + l32) * D + d0,
-                     &x[m][8 * g]);
+          const size_t at = ((static_cast<size_t>(hd) * Nb + ib) * 64 + 32 * w + l32) * D + d0;
+          load_f32x8(a.qt + at, &x[m][8 * g]);
+          if constexpr (SPLIT) {
+            float lo[8];
+            load_f32x8(a.qt_lo + at, lo);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[m][8 * g + e] += lo[e];
+          }
         } else if (pr >= 0) {
           load_f32x8(q + (static_cast<size_t>(pr) * H + hd) * D + d0, &x[m][8 * g]);
         } else {
@@ -331,16 +373,23 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
         qf8[m][j] = static_cast<int>(u);
       }
   } else if (a.qt) {
-    const uint16_t* qrow = a.qt + ((static_cast<size_t>(hd) * Nb + ib) * 64 + 32 * w + l32) * D;
+    const size_t at = ((static_cast<size_t>(hd) * Nb + ib) * 64 + 32 * w + l32) * D;
 #pragma unroll
-    for (int c = 0; c < NCK; ++c) qf[c] = IoOps<uint16_t>::load8(qrow + 16 * c + 8 * hl);
+    for (int c = 0; c < NCK; ++c) {
+      qf[c] = IoOps<uint16_t>::load8(a.qt + at + 16 * c + 8 * hl);
+      if constexpr (KSPLIT) qfl[c] = IoOps<uint16_t>::load8(a.qt_lo + at + 16 * c + 8 * hl);
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < NCK; ++c) {
-      if (pr >= 0)
-        qf[c] = IoOps<TIO>::load8(q + (static_cast<size_t>(pr) * H + hd) * D + 16 * c + 8 * hl);
-      else
+      if (pr >= 0) {
+        const TIO* src = q + (static_cast<size_t>(pr) * H + hd) * D + 16 * c + 8 * hl;
+        qf[c] = IoOps<TIO>::load8(src);
+        if constexpr (KSPLIT) qfl[c] = IoOps<float>::load8_lo(src);
+      } else {
         qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        if constexpr (KSPLIT) qfl[c] = qf[c];
+      }
     }
   }
 
@@ -350,6 +399,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   const char* ksh =
       QK8 ? reinterpret_cast<const char*>(a.kscale) + static_cast<size_t>(hd) * Nb * 256 : nullptr;
   const char* vth = reinterpret_cast<const char*>(a.vt) + static_cast<size_t>(hd) * Nb * V_TILE;
+  // Low parts (fp32 I/O): same layouts as Kt and Vt.
+  const char* ktl =
+      KSPLIT ? reinterpret_cast<const char*>(a.kt_lo) + static_cast<size_t>(hd) * Nb * K_TILE
+             : nullptr;
+  const char* vtl =
+      SPLIT ? reinterpret_cast<const char*>(a.vt_lo) + static_cast<size_t>(hd) * Nb * V_TILE
+            : nullptr;
   // Block of visit it.  Listed ids are clamped into [0, Nt): a corrupt list
   // can give a wrong result but never an out-of-bounds read.
   const int bmask = (1 << bsh) - 1;
@@ -380,54 +436,61 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
 // awaited explicitly (kWaitVm) before the barriers that publish a slot.  The
 // memory clobber keeps the compiler from moving memory accesses across it.
 #define VSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-// Half B of K tile J into slot SLOT: KH_LOADS loads per wave and, with QK8,
+// Half B of K tile J into slot SLOT: KH_LOADS loads per wave (per part: the
+// low parts of fp32 I/O follow the high parts at KH_BYTES) and, with QK8,
 // one load of 16 per-key scales by each of waves 0 and 1 (lanes 4..63 repeat
 // lanes 0..3).
 // Pad rows are zero in memory, so a loaded half holds no stale data; a half
 // without valid keys is neither loaded nor read.
 #define VSA_LOAD_KH(SLOT, J, B)                                                               \
   {                                                                                            \
-    const char* src_ = kth + static_cast<size_t>(J) * K_TILE + (B) * KH_BYTES;                 \
-    _Pragma("unroll") for (int e = 0; e < KH_LOADS; ++e) {                                     \
-      const int x_ = w * KH_LOADS + e;                                                         \
-      __builtin_amdgcn_global_load_lds(                                                        \
-          (gbl_void*)(src_ + kbase + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64),                  \
-          (lds_void*)((SLOT) + x_ * 1024), 16, 0, 0);                                          \
+    _Pragma("unroll") for (int p_ = 0; p_ < KPARTS; ++p_) {                                    \
+      const char* src_ = (p_ ? ktl : kth) + static_cast<size_t>(J) * K_TILE + (B) * KH_BYTES;  \
+      _Pragma("unroll") for (int e = 0; e < KH_LOADS; ++e) {                                   \
+        const int x_ = w * KH_LOADS + e;                                                       \
+        __builtin_amdgcn_global_load_lds(                                                      \
+            (gbl_void*)(src_ + kbase + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64),                \
+            (lds_void*)((SLOT) + p_ * KH_BYTES + x_ * 1024), 16, 0, 0);                        \
+      }                                                                                        \
     }                                                                                          \
     if (QK8 && w < 2)                                                                          \
       __builtin_amdgcn_global_load_lds(                                                        \
           (gbl_void*)(ksh + static_cast<size_t>(J) * 256 + 128 * (B) + 64 * w + 16 * (lane & 3)), \
           (lds_void*)((SLOT) + KH_BYTES + 1024 * w), 16, 0, 0);                                \
   }
-// Half B of V^T tile J into slot SLOT: VH_LOADS loads per wave.
+// Half B of V^T tile J into slot SLOT: VH_LOADS loads per wave and part.
 #define VSA_LOAD_VH(SLOT, J, B)                                                               \
   {                                                                                            \
-    const char* src_ = vth + static_cast<size_t>(J) * V_TILE + (B) * VH_BYTES;                 \
-    _Pragma("unroll") for (int e = 0; e < VH_LOADS; ++e) {                                     \
-      const int x_ = w * VH_LOADS + e;                                                         \
-      __builtin_amdgcn_global_load_lds((gbl_void*)(src_ + vbase + x_ * 1024),                  \
-                                       (lds_void*)((SLOT) + x_ * 1024), 16, 0, 0);             \
+    _Pragma("unroll") for (int p_ = 0; p_ < VPARTS; ++p_) {                                    \
+      const char* src_ = (p_ ? vtl : vth) + static_cast<size_t>(J) * V_TILE + (B) * VH_BYTES;  \
+      _Pragma("unroll") for (int e = 0; e < VH_LOADS; ++e) {                                   \
+        const int x_ = w * VH_LOADS + e;                                                       \
+        __builtin_amdgcn_global_load_lds((gbl_void*)(src_ + vbase + x_ * 1024),                \
+                                         (lds_void*)((SLOT) + p_ * VH_BYTES + x_ * 1024), 16,  \
+                                         0, 0);                                                \
+      }                                                                                        \
     }                                                                                          \
   }
   // Loads this wave issues for half b of a tile with n valid keys.
-  constexpr int CKMAX = KH_LOADS + (QK8 ? 1 : 0);
-  const int CK = KH_LOADS + (QK8 && w < 2 ? 1 : 0);
-  constexpr int CV = VH_LOADS;
-  static_assert(2 * (CKMAX > CV ? CKMAX : CV) <= 8, "wait counts above 8");
+  constexpr int CKMAX = KPARTS * KH_LOADS + (QK8 ? 1 : 0);
+  const int CK = KPARTS * KH_LOADS + (QK8 && w < 2 ? 1 : 0);
+  constexpr int CV = VPARTS * VH_LOADS;
+  static_assert(2 * (CKMAX > CV ? CKMAX : CV) <= 16, "wait counts above 16");
   auto ck = [CK](int n, int b) -> int { return n > 32 * b ? CK : 0; };
   auto cv = [](int n, int b) -> int { return n > 32 * b ? CV : 0; };
   // Wait until at most n of this wave's loads are in flight.
   auto wait_vm = [](int n) {
     switch (n) {
-      case 0: __builtin_amdgcn_s_waitcnt(kWaitVm | 0); break;
-      case 1: __builtin_amdgcn_s_waitcnt(kWaitVm | 1); break;
-      case 2: __builtin_amdgcn_s_waitcnt(kWaitVm | 2); break;
-      case 3: __builtin_amdgcn_s_waitcnt(kWaitVm | 3); break;
-      case 4: __builtin_amdgcn_s_waitcnt(kWaitVm | 4); break;
-      case 5: __builtin_amdgcn_s_waitcnt(kWaitVm | 5); break;
-      case 6: __builtin_amdgcn_s_waitcnt(kWaitVm | 6); break;
-      case 7: __builtin_amdgcn_s_waitcnt(kWaitVm | 7); break;
-      default: __builtin_amdgcn_s_waitcnt(kWaitVm | 8); break;
+#define VSA_WAIT_CASE(N) \
+  case N:                \
+    __builtin_amdgcn_s_waitcnt(wait_vm_imm(N)); \
+    break;
+      VSA_WAIT_CASE(1) VSA_WAIT_CASE(2) VSA_WAIT_CASE(3) VSA_WAIT_CASE(4) VSA_WAIT_CASE(5)
+      VSA_WAIT_CASE(6) VSA_WAIT_CASE(7) VSA_WAIT_CASE(8) VSA_WAIT_CASE(9) VSA_WAIT_CASE(10)
+      VSA_WAIT_CASE(11) VSA_WAIT_CASE(12) VSA_WAIT_CASE(13) VSA_WAIT_CASE(14)
+      VSA_WAIT_CASE(15) VSA_WAIT_CASE(16)
+#undef VSA_WAIT_CASE
+      default: __builtin_amdgcn_s_waitcnt(wait_vm_imm(0)); break;   // 0 (or, never, more)
     }
   };
 
@@ -484,7 +547,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
   constexpr int kQkSteps = QK8 ? NK64 : NCK;
   constexpr int kPvSteps = 2 * NB;
   constexpr int kAhead = 3;
-  typedef typename std::conditional<QK8, i32x8, bf16x8>::type QkOp;
+  typedef typename std::conditional<QK8, i32x8,
+                                    typename std::conditional<KSPLIT, Bf16Pair, bf16x8>::type>::type
+      QkOp;
+  typedef typename std::conditional<SPLIT, Bf16Pair, bf16x8>::type PvOp;
 
   // LDS operand of Q.K step k of half b (lane row l32 of the half's keys).
   auto qk_read = [&](int b, int k) -> QkOp {
@@ -496,9 +562,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
       const u32x4 k1 = *reinterpret_cast<const u32x4*>(g + (((2 * hl + 1) ^ rswz) << 4));
       return __builtin_bit_cast(i32x8, u32x8{k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w});
     } else {
-      // Chunk 2k + hl (channels 16k + 8hl + 0..7).
-      return *reinterpret_cast<const bf16x8*>(krow + (k >> 1) * 2048 +
-                                              (((2 * (k & 1) + hl) ^ rswz) << 4));
+      // Chunk 2k + hl (channels 16k + 8hl + 0..7); with fp32 I/O the low
+      // parts sit KH_BYTES further.
+      const char* c = krow + (k >> 1) * 2048 + (((2 * (k & 1) + hl) ^ rswz) << 4);
+      if constexpr (KSPLIT)
+        return Bf16Pair{*reinterpret_cast<const bf16x8*>(c),
+                        *reinterpret_cast<const bf16x8*>(c + KH_BYTES)};
+      else
+        return *reinterpret_cast<const bf16x8*>(c);
     }
   };
   // Q.K step k: S^T (keys x queries) of the half accumulates channels of step k.
@@ -507,6 +578,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
       // Scale bytes 127 (2^0): plain E4M3 x E4M3 products, fp32 sums.
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[k], k == 0 ? f32x16{} : acc,
                                                             0, 0, 0, 127, 0, 127);
+    } else if constexpr (KSPLIT) {
+      // k.q = k_hi.q_hi + k_lo.q_hi + k_hi.q_lo (fp32 sums).
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.h, qf[k], k == 0 ? f32x16{} : acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.l, qf[k], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.h, qfl[k], acc, 0, 0, 0);
     } else {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], k == 0 ? f32x16{} : acc, 0, 0, 0);
     }
@@ -529,18 +605,34 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
     }
   };
   // LDS operand of P.V step k of half b: V^T rows 32n.., 16-key group g of the half.
-  auto pv_read = [&](int b, int k) -> bf16x8 {
+  auto pv_read = [&](int b, int k) -> PvOp {
     const int g = k / NB, n = k % NB;
-    const char* vrow = (b ? lds_vb : lds_va) + (32 * n + l32) * 64;
-    return *reinterpret_cast<const bf16x8*>(vrow + (((2 * g + hl) ^ rswz) << 4));
+    const char* c = (b ? lds_vb : lds_va) + (32 * n + l32) * 64 + (((2 * g + hl) ^ rswz) << 4);
+    if constexpr (SPLIT)
+      return Bf16Pair{*reinterpret_cast<const bf16x8*>(c),
+                      *reinterpret_cast<const bf16x8*>(c + VH_BYTES)};
+    else
+      return *reinterpret_cast<const bf16x8*>(c);
   };
-  auto pv_step = [&](int k, const bf16x8& vf, const bf16x8& pa, const bf16x8& pb) {
+  // P.V step k; pa/pb the probabilities of the half's two 16-key groups,
+  // pal/pbl their low parts (fp32 I/O).
+  auto pv_step = [&](int k, const PvOp& vf, const bf16x8& pa, const bf16x8& pb,
+                     const bf16x8& pal, const bf16x8& pbl) {
     const int g = k / NB, n = k % NB;
-    oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, g == 0 ? pa : pb, oacc[n], 0, 0, 0);
+    if constexpr (SPLIT) {
+      // v.p = v_hi.p_hi + v_lo.p_hi + v_hi.p_lo (fp32 sums).
+      oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.h, g == 0 ? pa : pb, oacc[n], 0, 0, 0);
+      oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.l, g == 0 ? pa : pb, oacc[n], 0, 0, 0);
+      oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.h, g == 0 ? pal : pbl, oacc[n], 0, 0, 0);
+    } else {
+      oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, g == 0 ? pa : pb, oacc[n], 0, 0, 0);
+    }
   };
   // Softmax pairs [8k/NS, 8(k+1)/NS) of one half: p = exp2(s*scale - mref),
-  // packed to bf16 pair by pair (word r/2 of the two 16-key operands).
-  auto sm_part = [&](int k, int ns, const f32x16& sacc, float mref, uint32_t pw[8], float& ps) {
+  // packed to bf16 pair by pair (word r/2 of the two 16-key operands); with
+  // fp32 I/O also the low parts.
+  auto sm_part = [&](int k, int ns, const f32x16& sacc, float mref, uint32_t pw[8],
+                     uint32_t pwl[8], float& ps) {
 #pragma unroll
     for (int q = 8 * k / ns; q < 8 * (k + 1) / ns; ++q) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * q], scale_log2, -mref));
@@ -548,6 +640,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
       ps += p0;
       ps += p1;
       pw[q] = pack_bf16x2(p0, p1);
+      if constexpr (SPLIT) pwl[q] = pack_bf16x2_lo(p0, p1);
     }
   };
   // p <- bf16(p * f) for the 8 probabilities of one operand.
@@ -559,16 +652,32 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
     u.w = pack_bf16x2(__uint_as_float(u.w << 16) * f, __uint_as_float(u.w & 0xffff0000u) * f);
     p = __builtin_bit_cast(bf16x8, u);
   };
+  // The same for a two-part (hi + lo) operand: the scaled sum is split again.
+  auto rescale_split = [](bf16x8& ph, bf16x8& pl, float f) {
+    u32x4 h = __builtin_bit_cast(u32x4, ph);
+    u32x4 l = __builtin_bit_cast(u32x4, pl);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = (__uint_as_float(h[e] << 16) + __uint_as_float(l[e] << 16)) * f;
+      const float x1 =
+          (__uint_as_float(h[e] & 0xffff0000u) + __uint_as_float(l[e] & 0xffff0000u)) * f;
+      h[e] = pack_bf16x2(x0, x1);
+      l[e] = pack_bf16x2_lo(x0, x1);
+    }
+    ph = __builtin_bit_cast(bf16x8, h);
+    pl = __builtin_bit_cast(bf16x8, l);
+  };
   auto pack16 = [](const uint32_t pw[8], bf16x8& pa, bf16x8& pb) {
     pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
     pb = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
   };
   // Q.K of half b; if SM, the softmax of the other half (s_other, reference
-  // mref) is spread over the steps.  Returns that softmax's lane sum.
+  // mref) is spread over the steps, giving probabilities pa, pb (low parts
+  // pal, pbl with fp32 I/O).  Returns that softmax's lane sum.
   auto qk_phase = [&](int b, f32x16& acc, bool sm, const f32x16& s_other, float mref,
-                      bf16x8& pa, bf16x8& pb) -> float {
+                      bf16x8& pa, bf16x8& pb, bf16x8& pal, bf16x8& pbl) -> float {
     QkOp kf[kQkSteps];
-    uint32_t pv[8];
+    uint32_t pv[8], pvl[8];
     float ps = 0.0f;
 #pragma unroll
     for (int k = 0; k < kAhead && k < kQkSteps; ++k) kf[k] = qk_read(b, k);
@@ -577,19 +686,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
     for (int k = 0; k < kQkSteps; ++k) {
       if (k + kAhead < kQkSteps) kf[k + kAhead] = qk_read(b, k + kAhead);
       qk_step(k, kf[k], acc);
-      if (sm) sm_part(k, kQkSteps, s_other, mref, pv, ps);
+      if (sm) sm_part(k, kQkSteps, s_other, mref, pv, pvl, ps);
       __builtin_amdgcn_sched_barrier(0);
     }
     key_scales(b, acc);
-    if (sm) pack16(pv, pa, pb);
+    if (sm) {
+      pack16(pv, pa, pb);
+      if constexpr (SPLIT) pack16(pvl, pal, pbl);
+    }
     return ps;
   };
-  // P.V of half b (probabilities pa, pb); if SM, the softmax of s_other is
-  // spread over the steps.  Returns that softmax's lane sum.
-  auto pv_phase = [&](int b, const bf16x8& pa, const bf16x8& pb, bool sm, const f32x16& s_other,
-                      float mref, bf16x8& qa, bf16x8& qb) -> float {
-    bf16x8 vf[kPvSteps];
-    uint32_t pv[8];
+  // P.V of half b (probabilities pa, pb; low parts pal, pbl); if SM, the
+  // softmax of s_other is spread over the steps, giving qa, qb (qal, qbl).
+  // Returns that softmax's lane sum.
+  auto pv_phase = [&](int b, const bf16x8& pa, const bf16x8& pb, const bf16x8& pal,
+                      const bf16x8& pbl, bool sm, const f32x16& s_other, float mref, bf16x8& qa,
+                      bf16x8& qb, bf16x8& qal, bf16x8& qbl) -> float {
+    PvOp vf[kPvSteps];
+    uint32_t pv[8], pvl[8];
     float ps = 0.0f;
 #pragma unroll
     for (int k = 0; k < kAhead; ++k) vf[k] = pv_read(b, k);
@@ -597,11 +711,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
 #pragma unroll
     for (int k = 0; k < kPvSteps; ++k) {
       if (k + kAhead < kPvSteps) vf[k + kAhead] = pv_read(b, k + kAhead);
-      pv_step(k, vf[k], pa, pb);
-      if (sm) sm_part(k, kPvSteps, s_other, mref, pv, ps);
+      pv_step(k, vf[k], pa, pb, pal, pbl);
+      if (sm) sm_part(k, kPvSteps, s_other, mref, pv, pvl, ps);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (sm) pack16(pv, qa, qb);
+    if (sm) {
+      pack16(pv, qa, qb);
+      if constexpr (SPLIT) pack16(pvl, qal, qbl);
+    }
     return ps;
   };
   // Pad keys (index >= nj) of half b to -inf: key 32b + 8(r/4) + 4hl + r%4
@@ -666,10 +783,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
     if (has1) VSA_LOAD_VH(lds_vb, j, 1);
 
     f32x16 s0, s1;
-    bf16x8 pf[4];
+    bf16x8 pf[4], pfl[4];   // probabilities; low parts with fp32 I/O
     if (active) {
       // Phase 1.
-      qk_phase(0, s0, false, kNone, 0.0f, pf[0], pf[1]);
+      qk_phase(0, s0, false, kNone, 0.0f, pf[0], pf[1], pfl[0], pfl[1]);
       if (nj < 32) mask_half(s0, 0, nj);
       const float m0 = raised_max(max16(s0));
       if (m0 != m_run) {
@@ -689,12 +806,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
     if (active) {
       // Phase 2 (the pinned copy keeps the softmax inside the branch).
       if (has1) {
-        l_run += qk_phase(1, s1, true, s0, pinned(m_run), pf[0], pf[1]);
+        l_run += qk_phase(1, s1, true, s0, pinned(m_run), pf[0], pf[1], pfl[0], pfl[1]);
       } else {
-        uint32_t pv[8];
+        uint32_t pv[8], pvl[8];
         float ps = 0.0f;
-        sm_part(0, 1, s0, m_run, pv, ps);
+        sm_part(0, 1, s0, m_run, pv, pvl, ps);
         pack16(pv, pf[0], pf[1]);
+        if constexpr (SPLIT) pack16(pvl, pfl[0], pfl[1]);
         l_run += ps;
       }
       // The second half's max is settled before P.V of the first half starts.
@@ -721,13 +839,20 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
           l_run *= alpha1;
 #pragma unroll
           for (int n = 0; n < NB; ++n) oacc[n] *= alpha1;
-          rescale_bf16(pf[0], alpha1);
-          rescale_bf16(pf[1], alpha1);
+          if constexpr (SPLIT) {
+            rescale_split(pf[0], pfl[0], alpha1);
+            rescale_split(pf[1], pfl[1], alpha1);
+          } else {
+            rescale_bf16(pf[0], alpha1);
+            rescale_bf16(pf[1], alpha1);
+          }
         }
         // Phase 3.
-        l_run += pv_phase(0, pf[0], pf[1], true, s1, pinned(m_run), pf[2], pf[3]);
+        l_run += pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], true, s1, pinned(m_run), pf[2], pf[3],
+                          pfl[2], pfl[3]);
       } else {
-        pv_phase(0, pf[0], pf[1], false, kNone, 0.0f, pf[2], pf[3]);
+        pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], false, kNone, 0.0f, pf[2], pf[3], pfl[2],
+                 pfl[3]);
       }
     }
     // V^T half 1 of t landed; every wave is done with V^T half 0 of t.
@@ -737,7 +862,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_attn_kernel(FineArgs a,
 
     if (active && has1) {
       // Phase 4.
-      pv_phase(1, pf[2], pf[3], false, kNone, 0.0f, pf[2], pf[3]);
+      pv_phase(1, pf[2], pf[3], pfl[2], pfl[3], false, kNone, 0.0f, pf[2], pf[3], pfl[2], pfl[3]);
     }
     j = jn;
     nj = njn;

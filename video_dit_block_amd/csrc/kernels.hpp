@@ -12,6 +12,7 @@ struct QkPrepArgs {
   const float *cos, *sin;            // [L][D/2], packed token order
   float eps;
   uint16_t* qt;                      // [H][Nb][64][D] bf16: normalised, rotated q
+  uint16_t* qt_lo;                   // fp32 I/O: low bf16 parts of qt, or null
 };
 
 // Nt counts tiles; a tile is 1 << bsh blocks of 64 slots (bsh 0: 64-token
@@ -27,6 +28,9 @@ struct PermutePoolArgs {
   QkPrepArgs prep;
   uint8_t* kt8;                 // [H][Nb][64][D] E4M3 keys instead of kt, or null
   float* kscale;                // [H][Nb][64] per-key scale (with kt8)
+  // fp32 I/O: low parts lo = bf16(x - bf16(x)) of the keys (layout of kt; not
+  // with kt8) and values (layout of vt); null for bf16 I/O.
+  uint16_t *kt_lo, *vt_lo;
 };
 hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t stream);
 
@@ -80,6 +84,9 @@ struct FineArgs {
   const float* kscale;          // [H][Nb][64]
   int bsh, Pvis;
   const int32_t* order;         // [H][nchunks][Nt] dispatch order of query tiles (nchunks > 1)
+  // fp32 I/O: low bf16 parts of kt, vt and qt (each null where its high part
+  // is unused); every product is then formed from hi and lo terms.
+  const uint16_t *kt_lo, *vt_lo, *qt_lo;
 };
 hipError_t launch_fine(const FineArgs& a, hipStream_t stream);
 

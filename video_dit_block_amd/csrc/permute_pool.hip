@@ -31,6 +31,11 @@
 //   (a*c - b*s, a*s + b*c) with the token's cos/sin;
 // the results replace the staged rows (rounded to the I/O type), so pooling,
 // Kt and the tile-ordered copy of q (Qt, for the fine kernel) all use them.
+//
+// With fp32 I/O the tile-ordered operands are also written as low parts
+// lo = bf16(x - bf16(x)) next to the bf16 high parts (Kt_lo, Vt_lo, Qt_lo,
+// same layouts), so that the fine kernel can form fp32-accurate products from
+// bf16 matrix-core terms.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -52,7 +57,9 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
     const int32_t* __restrict__ perm, const int32_t* __restrict__ valid, int H, int Nt, int bsh,
     uint16_t* __restrict__ kt, uint16_t* __restrict__ vt, float* __restrict__ qp,
     float* __restrict__ kp, float* __restrict__ vp, QkPrepArgs prep, uint8_t* __restrict__ kt8,
-    float* __restrict__ kscale) {
+    float* __restrict__ kscale, uint16_t* __restrict__ kt_lo, uint16_t* __restrict__ vt_lo) {
+  // Low parts exist only for fp32 inputs.
+  constexpr bool kLo = sizeof(T) == 4;
   constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
   constexpr int kChunksPerRow = kRowBytes / 16;
   constexpr int kChunksPerTensor = 64 * kChunksPerRow;
@@ -213,15 +220,24 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
     // Kt (and Qt with PREP): [slot][d] bf16, 16-byte chunks of 8 channels.
     for (int x = PREP ? 0 : 1; x < (kt8 ? 1 : 2); ++x) {
       uint16_t* dst = (x == 0 ? prep.qt : kt) + tile_base * 64 * D;
+      uint16_t* dlo = (x == 0 ? prep.qt_lo : kt_lo) + tile_base * 64 * D;
       for (int c = tid; c < 64 * (D / 8); c += blockDim.x) {
         const int slot = c / (D / 8);
         const int d0 = (c - slot * (D / 8)) * 8;
+        const T* e = &lds[x][slot][d0];
         uint4 o;
-        o.x = pack_bf16x2(to_f32(lds[x][slot][d0 + 0]), to_f32(lds[x][slot][d0 + 1]));
-        o.y = pack_bf16x2(to_f32(lds[x][slot][d0 + 2]), to_f32(lds[x][slot][d0 + 3]));
-        o.z = pack_bf16x2(to_f32(lds[x][slot][d0 + 4]), to_f32(lds[x][slot][d0 + 5]));
-        o.w = pack_bf16x2(to_f32(lds[x][slot][d0 + 6]), to_f32(lds[x][slot][d0 + 7]));
+        o.x = pack_bf16x2(to_f32(e[0]), to_f32(e[1]));
+        o.y = pack_bf16x2(to_f32(e[2]), to_f32(e[3]));
+        o.z = pack_bf16x2(to_f32(e[4]), to_f32(e[5]));
+        o.w = pack_bf16x2(to_f32(e[6]), to_f32(e[7]));
         *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
+        if constexpr (kLo) {
+          o.x = pack_bf16x2_lo(e[0], e[1]);
+          o.y = pack_bf16x2_lo(e[2], e[3]);
+          o.z = pack_bf16x2_lo(e[4], e[5]);
+          o.w = pack_bf16x2_lo(e[6], e[7]);
+          *reinterpret_cast<uint4*>(dlo + static_cast<size_t>(slot) * D + d0) = o;
+        }
       }
     }
     // Vt: two halves of positions (0-31, 32-63), each [d][32] bf16 with
@@ -235,12 +251,20 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
         const int m = 4 * ((c >> 2) / D) + (c & 3);
         const int sa = 16 * (m >> 1) + 4 * (m & 1);
         const int sb = sa + 8;
+        const size_t at = static_cast<size_t>(m >> 2) * 32 * D + d * 32 + 8 * (m & 3);
         uint4 o;
         o.x = pack_bf16x2(to_f32(lds[2][sa + 0][d]), to_f32(lds[2][sa + 1][d]));
         o.y = pack_bf16x2(to_f32(lds[2][sa + 2][d]), to_f32(lds[2][sa + 3][d]));
         o.z = pack_bf16x2(to_f32(lds[2][sb + 0][d]), to_f32(lds[2][sb + 1][d]));
         o.w = pack_bf16x2(to_f32(lds[2][sb + 2][d]), to_f32(lds[2][sb + 3][d]));
-        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(m >> 2) * 32 * D + d * 32 + 8 * (m & 3)) = o;
+        *reinterpret_cast<uint4*>(dst + at) = o;
+        if constexpr (kLo) {
+          o.x = pack_bf16x2_lo(lds[2][sa + 0][d], lds[2][sa + 1][d]);
+          o.y = pack_bf16x2_lo(lds[2][sa + 2][d], lds[2][sa + 3][d]);
+          o.z = pack_bf16x2_lo(lds[2][sb + 0][d], lds[2][sb + 1][d]);
+          o.w = pack_bf16x2_lo(lds[2][sb + 2][d], lds[2][sb + 3][d]);
+          *reinterpret_cast<uint4*>(vt_lo + tile_base * 64 * D + at) = o;
+        }
       }
     }
     // Every read of this block's LDS rows is done before the next block's staging.
@@ -262,12 +286,12 @@ hipError_t launch(const PermutePoolArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((permute_pool_kernel<T, D, true>), grid, dim3(384), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.bsh, a.kt, a.vt,
-                       a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale);
+                       a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale, a.kt_lo, a.vt_lo);
   else
     hipLaunchKernelGGL((permute_pool_kernel<T, D, false>), grid, dim3(384), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.perm, a.valid, a.H, a.Nt, a.bsh, a.kt, a.vt,
-                       a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale);
+                       a.qp, a.kp, a.vp, a.prep, a.kt8, a.kscale, a.kt_lo, a.vt_lo);
   return hipGetLastError();
 }
 

@@ -81,6 +81,11 @@ void lay_out(vsa_h3_plan* plan) {
   lo.qt = take(plan->qk_prep ? h64 * nb64 * kTile * d64 * 2 : 0);
   lo.kt8 = take(plan->qk_fp8 ? h64 * nb64 * kTile * d64 : 0);
   lo.kscale = take(plan->qk_fp8 ? h64 * nb64 * kTile * 4 : 0);
+  // fp32 I/O: low bf16 parts of Kt (not with FP8 keys), Vt and Qt.
+  const uint64_t tok_bytes = h64 * nb64 * kTile * d64 * 2;
+  lo.kt_lo = take(plan->io_f32 && !plan->qk_fp8 ? tok_bytes : 0);
+  lo.vt_lo = take(plan->io_f32 ? tok_bytes : 0);
+  lo.qt_lo = take(plan->io_f32 && plan->qk_prep ? tok_bytes : 0);
   lo.total = off < 256 ? 256 : off;
   lo.ns = ns;
 }
@@ -121,6 +126,11 @@ vsa_status set_chunk_tiles(vsa_h3_plan* plan, int32_t chunk_tiles) {
 
 void set_qk_prep(vsa_h3_plan* plan, bool enable) {
   plan->qk_prep = enable;
+  lay_out(plan);
+}
+
+void set_io_f32(vsa_h3_plan* plan, bool f32) {
+  plan->io_f32 = f32;
   lay_out(plan);
 }
 

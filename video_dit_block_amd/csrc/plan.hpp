@@ -33,7 +33,7 @@ constexpr uint64_t kChunkBytesWide = uint64_t(32) << 20;
 
 struct Layout {
   uint64_t perm, valid, kt, vt, qp, kp, vp, scores, coarse, sel, choff, state, qt, kt8, kscale,
-      kind, visit, order, total;
+      kind, visit, order, kt_lo, vt_lo, qt_lo, total;
   int64_t ns;  // scores row stride
 };
 
@@ -69,6 +69,7 @@ struct vsa_h3_plan {
   int32_t num_chunks = 0;          // ceil(Nt / chunk_tiles); 0 when Nt == 0
   bool qk_prep = false;            // workspace holds Qt for the QK-norm + RoPE forward
   bool qk_fp8 = false;             // fine branch uses per-token FP8 q and k
+  bool io_f32 = false;             // laid out for fp32 I/O: low bf16 parts of K, V^T (and Qt)
   vsa::Layout layout{};
 };
 
@@ -92,6 +93,12 @@ void set_qk_prep(vsa_h3_plan* plan, bool enable);
 // Switches the fine branch to per-token FP8 (E4M3) q and k and adds the
 // regions of the quantised key tiles and their scales (or drops them).
 void set_qk_fp8(vsa_h3_plan* plan, bool enable);
+
+// Lays the workspace out for fp32 (true) or bf16 (false) I/O.  fp32 I/O
+// adds the low bf16 parts (x - bf16(x), rounded to bf16) of the tile-ordered
+// keys, values and, with QK-norm + RoPE, queries, so that the fine branch can
+// form fp32-accurate products from two bf16 terms.
+void set_io_f32(vsa_h3_plan* plan, bool f32);
 
 // Reference keep ratio in (0, 1]: below 1 each video query tile keeps only
 // its best-scoring reference (cond) key tiles; lays out the workspace again.
