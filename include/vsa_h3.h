@@ -317,6 +317,28 @@ vsa_status vsa_h3_plan_set_qk_fp8(vsa_h3_plan* plan, int32_t enable);
  * VSA_E_ARG if r is outside (0, 1] or NaN. */
 vsa_status vsa_h3_plan_set_ref_keep(vsa_h3_plan* plan, double keep);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * forward of vsa_h3_forward with the workspace taken from a device array
+ * inside the library instead of from the caller.  It calls no hipMalloc,
+ * hipFree or other allocating routine.
+ *   - The array holds 64 MiB on every GPU the library runs on, from the
+ *     first call on that GPU until the process ends.  A plan whose
+ *     workspace_bytes exceeds 64 MiB is refused with VSA_E_WORKSPACE (for
+ *     example the 480p 15,104-token layout fits at up to 7 heads).
+ *   - The device is the current one (hipGetDevice); the first call on a
+ *     device looks up that device's copy of the array.
+ *   - Each call first copies the plan's tables into the array on `stream`
+ *     (from host memory, as vsa_h3_plan_upload does), then runs the forward
+ *     there; nothing else in the array needs clearing.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind: calls that overlap in time on one GPU (other streams, other
+ *     threads) race and corrupt each other's results.  Serialize them.
+ * Arguments, outputs and errors as for vsa_h3_forward. */
+vsa_status vsa_h3_forward_noalloc(const vsa_h3_plan* plan, const void* q, const void* k,
+                                  const void* v, const void* gate, vsa_dtype io_dtype, void* out,
+                                  int32_t* sel_idx, void* stream);
+
 void vsa_h3_plan_destroy(vsa_h3_plan* plan);
 const char* vsa_h3_last_error(void);
 const char* vsa_h3_version(void);

@@ -30,6 +30,7 @@ from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
     vsa_h3_plan_layout, vsa_h3_plan_set_chunk_tiles, vsa_h3_plan_tables, vsa_h3_plan_upload,
     vsa_h3_topk, vsa_h3_version, vsa_h3_plan_set_qk_prep, vsa_h3_forward_qk_prep,
     vsa_h3_plan_set_qk_fp8, vsa_h3_plan_set_ref_keep, vsa_h3_plan_set_io_dtype,
+    vsa_h3_forward_noalloc,
 )
 
 __all__ = ["Plan", "forward", "forward_qk_prep", "VsaError", "vsa_h3_topk",

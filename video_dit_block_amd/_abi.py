@@ -27,6 +27,7 @@ EXPORTED = (
     "vsa_h3_oneshot_workspace_bytes", "vsa_h3_forward_oneshot", "vsa_h3_plan_destroy",
     "vsa_h3_last_error", "vsa_h3_version", "vsa_h3_plan_set_qk_prep", "vsa_h3_forward_qk_prep",
     "vsa_h3_plan_set_qk_fp8", "vsa_h3_plan_set_ref_keep", "vsa_h3_plan_set_io_dtype",
+    "vsa_h3_forward_noalloc",
 )
 
 
@@ -107,6 +108,7 @@ def lib() -> ctypes.CDLL:
         L.vsa_h3_plan_set_qk_fp8.argtypes = [_P, ctypes.c_int32]
         L.vsa_h3_plan_set_ref_keep.argtypes = [_P, ctypes.c_double]
         L.vsa_h3_plan_set_io_dtype.argtypes = [_P, ctypes.c_int]
+        L.vsa_h3_forward_noalloc.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P]
         L.vsa_h3_forward_qk_prep.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                              ctypes.c_int, _P, _P, _P, ctypes.c_uint64, _P,
                                              ctypes.POINTER(_P)]
@@ -198,6 +200,13 @@ def vsa_h3_forward_timed(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr
     arr = (_P * 4)(*events) if events is not None else None
     check(lib().vsa_h3_forward_timed(plan, q_ptr, k_ptr, v_ptr, gate_ptr, io_dtype, out_ptr,
                                      sel_ptr, workspace_ptr, workspace_bytes, stream, arr))
+
+
+def vsa_h3_forward_noalloc(plan: int, q_ptr: int, k_ptr: int, v_ptr: int, gate_ptr: int,
+                           io_dtype: int, out_ptr: int, sel_ptr, stream: int) -> None:
+    """The forward with the library's own device workspace (no allocation)."""
+    check(lib().vsa_h3_forward_noalloc(plan, q_ptr, k_ptr, v_ptr, gate_ptr, io_dtype, out_ptr,
+                                       sel_ptr, stream))
 
 
 def vsa_h3_plan_set_qk_prep(plan: int, enable: bool) -> None:

@@ -463,6 +463,75 @@ vsa_status vsa_h3_forward_oneshot(const void* q, const void* k, const void* v, c
                         stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of the forward that allocates nothing: one file-scope device
+// array, which each GPU the library runs on holds until the process ends.
+// Host code never passes the array's name to a kernel or a copy (on the host
+// it is only a stand-in symbol); it uses the device address that
+// hipGetSymbolAddress reports for the current device, looked up once per
+// device on the first call there.
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+vsa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail("hipGetDevice", err);
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device index " + std::to_string(dev) + " is beyond the " +
+              std::to_string(kMaxDevices) + " devices the no-allocation forward tracks");
+    return VSA_E_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", err);
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0) {
+      set_error("hipGetSymbolAddress(scratch) gave an unusable address");
+      return VSA_E_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vsa_status vsa_h3_forward_noalloc(const vsa_h3_plan* plan, const void* q, const void* k,
+                                  const void* v, const void* gate, vsa_dtype io_dtype, void* out,
+                                  int32_t* sel_idx, void* stream) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return VSA_E_ARG;
+  }
+  if (plan->layout.total > kScratchBytes) {
+    set_error("the plan needs a workspace of " + std::to_string(plan->layout.total) +
+              " bytes; the no-allocation forward holds at most " + std::to_string(kScratchBytes) +
+              " (use vsa_h3_forward with a caller-provided workspace)");
+    return VSA_E_WORKSPACE;
+  }
+  void* ws = nullptr;
+  vsa_status st = scratch_for_current_device(&ws);
+  if (st != VSA_OK) return st;
+  // The array keeps whatever the last call on this GPU left, so this call's
+  // plan tables go in first; nothing else in it has to start at zero (every
+  // other region is written before it is read within one forward).
+  st = vsa_h3_plan_upload(plan, ws, kScratchBytes, stream);
+  if (st != VSA_OK) return st;
+  return vsa_h3_forward(plan, q, k, v, gate, io_dtype, out, sel_idx, ws, kScratchBytes, stream);
+}
+
 void vsa_h3_plan_destroy(vsa_h3_plan* plan) { delete plan; }
 
 const char* vsa_h3_last_error(void) { return vsa::get_error(); }
