@@ -124,3 +124,37 @@ def check_dispatch_order(plan, ws, offsets, pvis):
             o = order[h, c]
             assert np.array_equal(np.sort(o), np.arange(Nt)), (h, c)
             assert np.all(np.diff(work[o]) <= 0), (h, c)
+
+
+def check_all_heads_selection(q_in, k_in, g, topk, qp_gpu, kp_gpu, sel_gpu, prep=None,
+                              threads=8):
+    """Pooled q/k and the selection of EVERY head bit-exact against the
+    oracle's fixed-order pool, scores and top-k (no fine branch), spread over
+    host threads (NumPy's array operations release the GIL).  q_in, k_in:
+    [L, H, D] inputs (torch or float32 NumPy); prep: the QK-norm + RoPE inputs
+    (CPU tensors) to apply per head first, with the R17 rounding for bf16."""
+    import concurrent.futures as cf
+    H = qp_gpu.shape[0]
+    is_bf16 = str(getattr(q_in, "dtype", "")).endswith("bfloat16")
+
+    def one(h):
+        qh = oracle.to_f32(q_in[:, h, :])
+        kh = oracle.to_f32(k_in[:, h, :])
+        if prep is not None:
+            def pr(x, wgt):
+                r = oracle.qk_norm_rope(x, wgt.numpy(), prep["eps"], prep["cos"].numpy(),
+                                        prep["sin"].numpy())
+                return (oracle.round_bf16_from_f64(r.astype(np.float64)).astype(np.float32)
+                        if is_bf16 else r)
+            qh, kh = pr(qh, prep["q_weight"]), pr(kh, prep["k_weight"])
+        qp = oracle.pool_canonical(qh, g)
+        kp = oracle.pool_canonical(kh, g)
+        sel = oracle.select_topk(oracle.scores_canonical(qp, kp), g, topk)
+        return (h, bool(np.array_equal(qp_gpu[h], qp)), bool(np.array_equal(kp_gpu[h], kp)),
+                bool(np.array_equal(sel_gpu[h], sel)))
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        res = list(ex.map(one, range(H)))
+    bad = [r for r in res if not all(r[1:])]
+    say(f"  selection and pooled q/k bit-exact on {H - len(bad)} of {H} heads")
+    assert not bad, bad[:4]

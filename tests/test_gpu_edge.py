@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_helpers import assert_close, intermediates, out_f64, require_gpu, run, say
+from tests.gpu_helpers import (F32_MAX_ABS, F32_REL_L2, assert_close, intermediates, out_f64,
+                               require_gpu, run, say)
 from workloads import TEXT, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -113,3 +114,67 @@ def test_one_token_video():
                          w.grid, w.sparsity)
     assert np.array_equal(sel.cpu().numpy()[:, :, 0], np.full((2, 1), 1))
     assert_close(out_f64(out), ref["out"], "one-token video")
+
+
+def _crafted_scores_inputs(values_per_head, seed):
+    """fp32 inputs whose pooled video-tile scores are exactly the given values:
+    every video query row is e0 (so each pooled query is e0); in video tile j
+    the first key row is 64 * values[h][j] * e0 and the other rows are zero, so
+    the fixed-order sum is exact and the pooled key is values[h][j] * e0, and
+    the fixed-order score of any video query tile against it is values[h][j]
+    (a product of +-0 adds to the +0 start as +0)."""
+    H = len(values_per_head)
+    w = Workload("crafted", H, 64, "f32", ((TEXT, 64),), (8, 8, 16), 0.5)   # 1 + 16 tiles, topk 8
+    x = make_inputs(w, seed=seed)
+    g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
+    assert g.NV == 16
+    for j in range(g.P, g.Nt):
+        rows = torch.as_tensor(g.tiles[j])
+        x["q"][rows] = 0.0
+        x["q"][rows, :, 0] = 1.0
+        x["k"][rows] = 0.0
+        for h in range(H):
+            x["k"][rows[0], h, 0] = 64.0 * float(values_per_head[h][j - g.P])
+    return w, x, g
+
+
+def test_topk_ties_straddling_the_kth_rank_low_bit_decisions_and_zero_scores():
+    """Selections decided by the top-k kernel's hardest cases: a cluster of
+    equal scores straddling the k-th rank (lower indices win), the k-th and
+    (k+1)-th scores differing only in the last bit of the fp32 mantissa (the
+    bitwise search reaches count == k only there), every score equal, and a
+    cluster of zero scores (from keys of either sign of zero) around the k-th
+    rank."""
+    u = 2.0 ** -23
+    perm = np.random.default_rng(3).permutation(16)
+    vals = [
+        # 2 scores of 3, then 7 of 2 at scattered indices: 6 of the 2s fit
+        [2, 1, 3, 2, 0.5, 2, 1, 2, 3, 2, -1, 2, 0.25, 2, 1, 0],
+        # 1 + m*2^-23 for m = 13..28: kept m = 21..28; 21 and 20 differ in bit 0 only
+        [1.0 + (13 + int(m)) * u for m in perm],
+        # all equal: the 8 lowest indices
+        [1.5] * 16,
+        # 10 zeros of either sign, 6 negatives: the 8 lowest-indexed zeros
+        [-0.0, 0.0, -1, 0.0, -0.0, -2, 0.0, -0.5, -0.0, 0.0, -3, -0.0, 0.0, -0.25, -4, -8],
+    ]
+    w, x, g = _crafted_scores_inputs(vals, seed=17)
+    out, sel, plan, ws = run(x, w.grid, w.sparsity)
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["gate"], x["token_tags"], x["position_ids"],
+                         w.grid, w.sparsity)
+    inter = intermediates(plan, ws)
+    want = [
+        [0, 2, 3, 5, 7, 8, 9, 11],
+        sorted(int(j) for j in np.nonzero(perm + 13 >= 21)[0]),
+        list(range(8)),
+        [0, 1, 3, 4, 6, 8, 9, 11],
+    ]
+    # the k-th and (k+1)-th scores of head 1 differ in the last mantissa bit only
+    top = np.sort(np.float32(vals[1]))[::-1]
+    assert int(top[7].view(np.uint32)) ^ int(top[8].view(np.uint32)) == 1
+    sel_h = sel.cpu().numpy()
+    for h in range(w.heads):
+        assert np.array_equal(inter["kp"][h, g.P:, 0], np.float32(vals[h])), h
+        assert np.array_equal(ref["heads"][h].sel[0], np.array(want[h]) + g.P), h   # oracle
+        assert np.array_equal(sel_h[h], ref["heads"][h].sel), h                     # GPU
+        assert (sel_h[h] == sel_h[h][0]).all(), h     # every query tile ties the same way
+    assert_close(out_f64(out), ref["out"], "crafted scores", F32_MAX_ABS, F32_REL_L2)

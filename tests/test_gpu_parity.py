@@ -14,8 +14,9 @@ import torch
 
 import oracle
 import video_dit_block_amd as vsa
-from tests.gpu_helpers import (F32_MAX_ABS, F32_REL_L2, assert_close, check_dispatch_order,
-                               errors, intermediates, out_f64, require_gpu, run, say)
+from tests.gpu_helpers import (F32_MAX_ABS, F32_REL_L2, assert_close, check_all_heads_selection,
+                               check_dispatch_order, errors, intermediates, out_f64, require_gpu,
+                               run, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -254,6 +255,8 @@ def sampled_check(name, heads):
     assert sel_all.min() >= g.P and sel_all.max() < g.Nt
     assert torch.isfinite(out).all()
     inter = intermediates(plan, ws)
+    # every head: pooled q/k and the selection, bit for bit
+    check_all_heads_selection(x["q"], x["k"], g, topk, inter["qp"], inter["kp"], sel_all)
     rng = np.random.default_rng(123)
     for h in heads:
         r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, h, with_fine=False)

@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_helpers import (assert_close, errors, intermediates, oracle_prep, out_f64,
+from tests.gpu_helpers import (assert_close, check_all_heads_selection, errors, intermediates,
+                               oracle_prep, out_f64,
                                require_gpu, run, run_qk_prep, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs, make_qk_prep_inputs
 
@@ -116,6 +117,8 @@ def test_qk_fp8_768p10s_sampled():
     topk = plan.topk
     inter = intermediates(plan, ws)
     sel_all = sel.cpu().numpy()
+    # every head: pooled q/k and the selection, bit for bit (FP8 touches neither)
+    check_all_heads_selection(x["q"], x["k"], g, topk, inter["qp"], inter["kp"], sel_all)
     rng = np.random.default_rng(3)
     scale = 1.0 / math.sqrt(w.head_dim)
     for h in (0, 50):

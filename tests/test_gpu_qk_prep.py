@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_helpers import (assert_close, errors, intermediates, oracle_prep, out_f64,
+from tests.gpu_helpers import (assert_close, check_all_heads_selection, errors, intermediates,
+                               oracle_prep, out_f64,
                                require_gpu, run_qk_prep, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs, make_qk_prep_inputs
 
@@ -114,6 +115,9 @@ def test_qk_prep_768p10s_sampled():
     g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid)
     inter = intermediates(plan, ws)
     sel_all = sel.cpu().numpy()
+    # every head: the prepared q/k's pooled values and the selection, bit for bit
+    check_all_heads_selection(x["q"], x["k"], g, plan.topk, inter["qp"], inter["kp"], sel_all,
+                              prep=prep)
     import math
     rng = np.random.default_rng(5)
     for h in (0, 41):

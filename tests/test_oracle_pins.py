@@ -558,6 +558,52 @@ def test_rope_rotates_adjacent_channel_pairs_of_the_input():
         assert np.array_equal(z[:, 2 * i + 1], y[:, 2 * i])
 
 
+def test_prep_qk_per_head_weights_rotation_and_io_rounding_closed_form():
+    """prep_qk's own steps (R14-R17 over every head): q uses q_weight and k uses
+    k_weight, each head and token separately, and the result is rounded to the
+    I/O dtype -- bf16 nearest-even for bf16 inputs, left exact for fp32 ones.
+    Rows of +-s (s a power of two) normalise to exactly +-1 with eps 0, so the
+    expected values follow by hand: y_d = sign_d * w_d, then the token's turn
+    of each pair (identity, a quarter turn of pair 0, a half turn)."""
+    u = 2.0 ** -10
+    qw = np.array([1 + u, 1.5, 3.0, 1 + 2 ** -8 + u], np.float32)      # not all bf16 values
+    kw = np.array([2.0, 1 + 2 ** -9, 0.75, 1.0 + 2 ** -7], np.float32)
+    sign = np.array([[1.0, -1.0, 1.0, 1.0], [-1.0, 1.0, 1.0, -1.0]])    # per head
+    L, H, D = 3, 2, 4
+    scale = np.array([[0.5, 4.0], [2.0, 0.125], [1.0, 8.0]])           # per token and head
+    x = (scale[:, :, None] * sign[None, :, :]).astype(np.float32)
+    cos = np.array([[1, 1], [0, 1], [-1, -1]], np.float32)             # [L, D/2]
+    sin = np.array([[0, 0], [1, 0], [0, 0]], np.float32)
+
+    def by_hand(w):
+        out = np.empty((L, H, D))
+        for h in range(H):
+            y = sign[h] * w.astype(np.float64)                         # normalised and weighted
+            out[0, h] = y                                              # identity
+            out[1, h] = [-y[1], y[0], y[2], y[3]]                      # pair 0 quarter turn
+            out[2, h] = -y                                             # half turn of both pairs
+        return out
+
+    def bf16_by_hand(v):
+        # nearest-even to 8 significant bits, written out for these magnitudes
+        m, e = np.frexp(np.abs(v))
+        return np.sign(v) * np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+    q32, k32 = oracle.prep_qk(x, x * 3.0, qw, kw, 0.0, cos, sin)
+    assert q32.dtype == np.float32 and q32.shape == (L, H, D)
+    assert np.array_equal(q32, by_hand(qw))                            # fp32: exact, no rounding
+    assert np.array_equal(k32, by_hand(kw))                            # k: its own weights
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    assert torch.equal(xb.float(), torch.from_numpy(x))                # inputs exact in bf16
+    qb, kb = oracle.prep_qk(xb, xb, qw, kw, 0.0, cos, sin)
+    want_q = bf16_by_hand(by_hand(qw))
+    assert np.array_equal(qb, want_q)
+    assert np.array_equal(kb, bf16_by_hand(by_hand(kw)))
+    # the rounding decided these: 1 + 2^-10 -> 1, 1 + 2^-8 + 2^-10 -> 1 + 2^-7 (above the tie)
+    assert want_q[0, 0, 0] == 1.0 and want_q[0, 0, 3] == 1 + 2 ** -7
+    assert kb[0, 0, 1] == -1.0 and kb[0, 1, 1] == 1.0                  # +-(1 + 2^-9) -> +-1
+
+
 # ----------------------------------------------------------------- FP8 (OCP E4M3) Q/K for the fine branch
 def test_e4m3_decode_printed_codes():
     # values fixed by the OCP FP8 definition: bias 7, 3 mantissa bits, subnormals, max 448
