@@ -354,3 +354,39 @@ def test_fp32_io_plan_regions_and_errors():
                                              w.sparsity, vsa.VSA_F32)
     assert (n16, n32) == (base, vsa.Plan(tags, pos, w.grid, H, D, w.sparsity,
                                          io_dtype="f32").workspace_bytes)
+
+
+def test_plan_cache_is_bounded_by_workspace_bytes():
+    # workspaces stand in as host tensors (no GPU here): the cache evicts the
+    # least recently used plans until what it pins fits the byte budget
+    import torch
+    old = vsa.plan_cache_bytes()
+    vsa._plans.clear()
+    try:
+        vsa.set_plan_cache_bytes(2500)
+        plans = []
+        for n in range(3):
+            w = Workload(f"c{n}", 2, 64, "f32", ((TEXT, 10 + n),), (4, 4, 4), 0.5)
+            tags, pos = make_layout(w)
+            p = vsa.get_plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity)
+            p._ws[(0, n)] = torch.empty(1000, dtype=torch.uint8)
+            plans.append(p)
+            vsa._trim_plan_cache()
+        cached = list(vsa._plans.values())
+        assert cached == plans[1:]                      # the oldest went first
+        assert sum(p.resident_bytes() for p in cached) <= 2500
+        # a plan used again moves to the back of the eviction order
+        w = Workload("c1", 2, 64, "f32", ((TEXT, 11),), (4, 4, 4), 0.5)
+        tags, pos = make_layout(w)
+        assert vsa.get_plan(tags, pos, w.grid, w.heads, w.head_dim, w.sparsity) is plans[1]
+        vsa.set_plan_cache_bytes(1500)
+        assert list(vsa._plans.values()) == [plans[1]]
+        # a plan whose own workspaces exceed the budget is not kept either
+        plans[1]._ws[(0, 9)] = torch.empty(1000, dtype=torch.uint8)
+        vsa._trim_plan_cache()
+        assert not vsa._plans
+        with pytest.raises(vsa.VsaError):
+            vsa.set_plan_cache_bytes(-1)
+    finally:
+        vsa._plans.clear()
+        vsa.set_plan_cache_bytes(old)

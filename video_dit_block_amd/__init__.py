@@ -16,7 +16,9 @@ device memory and the stream).
 """
 from __future__ import annotations
 
+import contextlib
 import hashlib
+import os
 import threading
 from collections import OrderedDict
 
@@ -34,7 +36,8 @@ from ._abi import (  # noqa: F401  (re-exported: same names as the C ABI)
 )
 
 __all__ = ["Plan", "forward", "forward_qk_prep", "VsaError", "vsa_h3_topk",
-           "vsa_h3_version", "io_dtype_code"] + list(EXPORTED)
+           "vsa_h3_version", "io_dtype_code", "get_plan", "plan_cache_bytes",
+           "set_plan_cache_bytes"] + list(EXPORTED)
 
 
 def io_dtype_code(dtype) -> int:
@@ -131,20 +134,43 @@ class Plan:
         return vsa_h3_plan_tables(self.handle)
 
     def workspace(self, device, stream=None):
-        """The plan's workspace on ``device`` (a torch uint8 tensor), created and
-        filled with the plan's tables on first use."""
+        """The plan's workspace for work on ``stream`` (a raw stream handle;
+        default: the device's current stream) of ``device``: a torch uint8
+        tensor, created and filled with the plan's tables on first use.
+
+        Every (device, stream) pair has its own workspace, so forwards that
+        share this plan on different streams never share scratch memory.  It
+        is allocated with that stream current, so once the plan lets go of it
+        (``release_workspaces``, or the plan cache evicting the plan) the
+        caching allocator hands the memory out again only in that stream's
+        order, after the forwards already queued there."""
         import torch
         device = torch.device(device)
-        key = device.index if device.index is not None else torch.cuda.current_device()
+        dev = device.index if device.index is not None else torch.cuda.current_device()
+        cur = torch.cuda.current_stream(dev)
+        s = cur.cuda_stream if stream is None else int(stream)
+        key = (dev, s)
         with self._ws_lock:
             ws = self._ws.get(key)
             if ws is None:
-                ws = torch.empty(self.workspace_bytes, dtype=torch.uint8,
-                                 device=torch.device("cuda", key))
-                s = stream if stream is not None else torch.cuda.current_stream(key).cuda_stream
+                cuda = torch.device("cuda", dev)
+                ctx = (contextlib.nullcontext() if s == cur.cuda_stream else
+                       torch.cuda.stream(torch.cuda.ExternalStream(s, device=cuda)))
+                with ctx:
+                    ws = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=cuda)
                 vsa_h3_plan_upload(self.handle, ws.data_ptr(), self.workspace_bytes, s)
                 self._ws[key] = ws
             return ws
+
+    def resident_bytes(self) -> int:
+        """Device bytes held by this plan's workspaces."""
+        with self._ws_lock:
+            return sum(int(w.numel()) for w in self._ws.values())
+
+    def release_workspaces(self) -> None:
+        """Drop every workspace (each is freed in its own stream's order)."""
+        with self._ws_lock:
+            self._ws.clear()
 
     def view(self, ws, name: str, dtype, shape):
         """A typed view of one workspace region (for tests and tools)."""
@@ -166,11 +192,46 @@ class Plan:
 
 _plans: "OrderedDict[tuple, Plan]" = OrderedDict()
 _plans_lock = threading.Lock()
+_PLAN_CACHE_MAX_PLANS = 8
+_plan_cache_bytes = int(os.environ.get("VSA_H3_PLAN_CACHE_BYTES", 16 << 30))
+
+
+def plan_cache_bytes() -> int:
+    """Most device bytes the workspaces of cached plans may hold between calls."""
+    return _plan_cache_bytes
+
+
+def set_plan_cache_bytes(n: int) -> None:
+    """Set the byte budget of the plan cache (default 16 GiB, or the
+    VSA_H3_PLAN_CACHE_BYTES environment variable) and trim the cache to it."""
+    global _plan_cache_bytes
+    if int(n) < 0:
+        raise VsaError(-1, "the plan cache budget must be >= 0 bytes")
+    _plan_cache_bytes = int(n)
+    _trim_plan_cache()
+
+
+def _trim_plan_cache() -> None:
+    """Evict least recently used plans until the cache holds at most
+    _PLAN_CACHE_MAX_PLANS plans whose workspaces total at most the byte
+    budget.  A plan is evicted whole: the cache drops its reference, and its
+    workspaces are freed once no caller holds the plan either."""
+    with _plans_lock:
+        sizes = {key: p.resident_bytes() for key, p in _plans.items()}
+        total = sum(sizes.values())
+        for key in list(_plans):
+            if total <= _plan_cache_bytes and len(_plans) <= _PLAN_CACHE_MAX_PLANS:
+                break
+            total -= sizes[key]
+            del _plans[key]
 
 
 def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4, 4, 4),
              qk_prep: bool = False, ref_keep: float = 1.0, io_dtype="bf16") -> Plan:
-    """Cached Plan for this exact layout (keyed by a digest of tags and positions)."""
+    """Cached Plan for this exact layout (keyed by a digest of tags and
+    positions).  The cache keeps at most 8 plans, and between calls their
+    workspaces hold at most ``plan_cache_bytes()`` of device memory: the
+    forward calls trim it once their work is queued."""
     tags = _host_i64(token_tags).reshape(-1)
     pos = _host_i64(position_ids).reshape(-1, 3)
     digest = hashlib.sha256(tags.tobytes() + b"|" + pos.tobytes()).hexdigest()
@@ -185,9 +246,9 @@ def get_plan(token_tags, position_ids, grid, heads, head_dim, sparsity, tile=(4,
     p = Plan(tags, pos, grid, heads, head_dim, sparsity, tile, qk_prep=qk_prep,
              ref_keep=ref_keep, io_dtype=io)
     with _plans_lock:
-        _plans[key] = p
-        while len(_plans) > 8:
-            _plans.popitem(last=False)
+        p = _plans.setdefault(key, p)
+        _plans.move_to_end(key)
+    _trim_plan_cache()
     return p
 
 
@@ -235,6 +296,7 @@ def forward(q, k, v, gate, token_tags=None, position_ids=None, grid=None, sparsi
     vsa_h3_forward(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), io,
                    out.data_ptr(), sel.data_ptr() if sel is not None and sel.numel() else None,
                    ws.data_ptr(), plan.workspace_bytes, stream)
+    _trim_plan_cache()
     return (out, sel) if return_sel else out
 
 
@@ -290,4 +352,5 @@ def forward_qk_prep(q, k, v, gate, q_norm_weight, k_norm_weight, eps, rope_cos, 
                            out.data_ptr(),
                            sel.data_ptr() if sel is not None and sel.numel() else None,
                            ws.data_ptr(), plan.workspace_bytes, stream)
+    _trim_plan_cache()
     return (out, sel) if return_sel else out
