@@ -14,7 +14,10 @@ own selection) plus the coarse branch, divided by the measured time per
 forward.  ``roofline`` covers the dominant kernel (fine attention) from HIP
 events recorded on the kernels' stream around each launch; ``cpu_baseline``
 times the CPU oracle on one head of the same workload (a bounded sample) and
-also checks the GPU output of that head against it.
+also checks the GPU output of that head against it.  ``configs`` repeats the
+measurement on the other workloads (480p 5 s, the structured 768p 10-s and
+15-s clips at sparsity 0.9, the OmniRef profile), each with its head-0 parity
+against the oracle.
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -37,6 +41,10 @@ METRIC = "VSA-H3 fwd ms and effective TFLOP/s (% bf16 MFMA peak) at 73.6k tokens
 FINE_SOURCES = ["video_dit_block_amd/csrc/fine_attn.hip", "video_dit_block_amd/csrc/device.hpp",
                 "video_dit_block_amd/csrc/kernels.hpp", "video_dit_block_amd/csrc/plan.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_{workload}_traffic.json")
+# Timed after the headline workload and reported in the configs array: the
+# 480p 5-s clip, the 768p 10-s and 15-s clips with structured q/k at sparsity
+# 0.9, and the OmniRef profile (128-token tiles, reference keep 0.1).
+EXTRA_WORKLOADS = ("480p5s", "768p10s_smooth", "768p15s_smooth", "omniref768p10s")
 
 
 def log(*a):
@@ -171,83 +179,108 @@ def load_traffic(launches: int, workload: str, chunk_tiles: int):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(x, w, gpu_out, gpu_sel, plan, head=0):
-    """Time the oracle (as it stands) on one head of the workload and check the
-    GPU's output and selection for that head against it."""
-    import oracle
+def host_cpu() -> dict:
+    """The host's logical CPU count, CPU model and the thread counts of the
+    BLAS and OpenMP pools the oracle's NumPy calls run on."""
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    pools = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = [{"api": i.get("user_api"), "library": i.get("internal_api"),
+                  "threads": int(i.get("num_threads", 1))} for i in threadpool_info()]
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
+    blas = [p["threads"] for p in pools if p["api"] == "blas"]
+    return {"host_cpus": os.cpu_count(), "cpu_model": model,
+            "blas_threads": max(blas) if blas else None, "thread_pools": pools}
+
+
+def oracle_head(x, w, head=0):
+    """The oracle's whole forward of one head, with the seconds of each step."""
+    import oracle
     g = oracle.geometry(x["token_tags"], x["position_ids"], w.grid, w.tile)
     topk = oracle.topk_count(g.NV, w.sparsity)
+    stages = {}
     t0 = time.perf_counter()
     r = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g, topk, head,
-                            ref_keep=w.ref_keep)
-    t1 = time.perf_counter()
-    if r.ref_sel is None:
-        sel_o, fixed = r.sel, None
-    else:
-        sel_o = np.concatenate([r.ref_sel, r.sel], axis=1)
-        fixed = np.nonzero(g.tile_tag[:g.P] != oracle.COND)[0]
-    alg, _ = fine_flops(sel_o[None].astype(np.int64), g.valid, g.P, g.L, w.head_dim, fixed,
-                        g.tile_tokens)
-    flops = alg + 4.0 * w.head_dim * g.Nt ** 2
+                            ref_keep=w.ref_keep, timings=stages)
+    return g, r, time.perf_counter() - t0, stages
+
+
+def head_parity(g, r, gpu_out, gpu_sel, head=0):
+    """Selection (bit-exact) and output error of one head against the oracle."""
+    import oracle
+    sel_o = r.sel if r.ref_sel is None else np.concatenate([r.ref_sel, r.sel], axis=1)
     ref = oracle.round_bf16_from_f64(r.out)
     got = gpu_out[:, head, :].to("cpu").double().numpy()
     d = got - ref
-    parity = {"head": head, "sel_bit_exact": bool(np.array_equal(gpu_sel[head], sel_o)),
-              "max_abs": float(np.abs(d).max()),
-              "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref))}
-    return {"value": flops / (t1 - t0) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": t1 - t0,
-            "sample": f"head {head} of {w.heads} of the {w.name} workload (whole per-head forward: "
-                      "pool, scores, top-k, coarse, float64 fine branch, combine)"}, parity
+    return sel_o, {"head": head, "sel_bit_exact": bool(np.array_equal(gpu_sel[head], sel_o)),
+                   "max_abs": float(np.abs(d).max()),
+                   "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref)),
+                   "bar": {"max_abs": 2e-2, "rel_l2": 5e-3}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="768p10s",
-                    help="a workload name from workloads.WORKLOADS, e.g. omniref768p10s "
-                         "(128-token tiles, reference keep 0.1)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--chunk-tiles", type=int, default=0,
-                    help="key tiles per fine-branch key chunk (0: the library's default)")
-    ap.add_argument("--qk-fp8", action="store_true",
-                    help="time the forward with per-token FP8 (E4M3) q and k in the fine branch")
-    ap.add_argument("--qk-prep", action="store_true",
-                    help="time the forward with QK RMS norm + RoPE fused into the gather "
-                         "(synthetic weights and cos/sin tables)")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="counter runs: one 1 GiB device copy (traffic calibration), then the "
-                         "warmup and timed forwards; no CPU baseline")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the forward is single-GPU; multi-GPU sharding is a design note only)",
-              file=sys.stderr)
-        sys.exit(2)
+def oracle_flops(g, sel_o, w, head_dim):
+    import oracle
+    fixed = None
+    if sel_o.shape[1] != oracle.topk_count(g.NV, w.sparsity):
+        fixed = np.nonzero(g.tile_tag[:g.P] != oracle.COND)[0]
+    alg, _ = fine_flops(sel_o[None].astype(np.int64), g.valid, g.P, g.L, head_dim, fixed,
+                        g.tile_tokens)
+    return alg + 4.0 * head_dim * g.Nt ** 2
 
-    import torch
-    sys.path.insert(0, ROOT)
-    import video_dit_block_amd as vsa
-    from workloads import WORKLOADS, make_inputs, make_qk_prep_inputs
 
-    w = WORKLOADS[args.workload]
-    log(f"bench: workload {w.name}: {w.description}")
+def cpu_baseline(x, w, gpu_out, gpu_sel, head=0):
+    """Time the oracle (as it stands) on one head of the workload and check the
+    GPU's output and selection for that head against it."""
+    hc = host_cpu()
+    g, r, secs, stages = oracle_head(x, w, head)
+    sel_o, parity = head_parity(g, r, gpu_out, gpu_sel, head)
+    flops = oracle_flops(g, sel_o, w, w.head_dim)
+    cb = {"value": flops / secs / 1e12, "unit": "TFLOP/s",
+          # the float64 fine branch (all but a few % of the time) is BLAS
+          # matrix products; the other steps run on one thread
+          "cores": hc["blas_threads"] or 1,
+          "kind": "oracle", "seconds": secs,
+          "sample": f"head {head} of {w.heads} of the {w.name} workload (whole per-head forward: "
+                    "pool, scores, top-k, coarse, float64 fine branch, combine); value = that "
+                    "head's effective flops over its wall time",
+          "host_cpus": hc["host_cpus"], "cpu_model": hc["cpu_model"],
+          "blas_threads": hc["blas_threads"], "thread_pools": hc["thread_pools"],
+          "stage_s": {k: round(v, 4) for k, v in stages.items()}}
+    return cb, parity
+
+
+def run_forward(w, args, torch, vsa, dev, qk_prep=False, qk_fp8=False, chunk_tiles=0,
+                calibrate=False):
+    """Seeded inputs of workload w in HBM, one plan, W untimed and K timed
+    forwards with HIP events around each stage.  Returns the pieces the
+    reports need."""
+    from workloads import make_inputs, make_qk_prep_inputs
     t = time.perf_counter()
     x = make_inputs(w, seed=0)
-    log(f"bench: inputs generated in {time.perf_counter() - t:.1f}s")
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
+    log(f"bench: {w.name}: inputs generated in {time.perf_counter() - t:.1f}s")
     xd = {n: x[n].to(dev) for n in ("q", "k", "v", "gate")}
     plan = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim, w.sparsity,
-                    w.tile, chunk_tiles=args.chunk_tiles, qk_prep=args.qk_prep,
-                    qk_fp8=args.qk_fp8, ref_keep=w.ref_keep)
+                    w.tile, chunk_tiles=chunk_tiles, qk_prep=qk_prep, qk_fp8=qk_fp8,
+                    ref_keep=w.ref_keep)
     stream = torch.cuda.current_stream(dev)
     ws = plan.workspace(dev, stream.cuda_stream)
     out = torch.empty_like(xd["q"])
@@ -256,7 +289,7 @@ def main():
     io = vsa.VSA_BF16 if w.io_dtype == "bf16" else vsa.VSA_F32
     ptrs = [xd[n].data_ptr() for n in ("q", "k", "v", "gate")]
 
-    if args.profile_pass:
+    if calibrate:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -267,13 +300,12 @@ def main():
 
     hip = HipEvents()
     evs = [hip.create(4) for _ in range(args.steps)]
-
-    if args.qk_prep:
+    if qk_prep:
         prep = make_qk_prep_inputs(w, x["position_ids"])
         pd = {n: prep[n].to(dev) for n in ("q_weight", "k_weight", "cos", "sin")}
 
     def step(events=None):
-        if args.qk_prep:
+        if qk_prep:
             vsa.vsa_h3_forward_qk_prep(plan.handle, *ptrs, pd["q_weight"].data_ptr(),
                                        pd["k_weight"].data_ptr(), prep["eps"],
                                        pd["cos"].data_ptr(), pd["sin"].data_ptr(), io,
@@ -287,7 +319,6 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"bench: {args.warmup} warmup steps done")
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(evs[s])
@@ -298,7 +329,7 @@ def main():
     event_ms = np.array([hip.elapsed_ms(e[0], e[3]) for e in evs])
     for e in evs:
         hip.destroy(e)
-    log(f"bench: {args.steps} timed steps, {ms_per_step:.3f} ms/step (wall), "
+    log(f"bench: {w.name}: {args.steps} timed steps, {ms_per_step:.3f} ms/step (wall), "
         f"{event_ms.mean():.3f} ms/step (events)")
 
     perm, valid, _ = plan.tables()
@@ -307,19 +338,99 @@ def main():
     alg_fine, padded_fine = fine_flops(sel_h.astype(np.int64), valid, plan.num_prefix_tiles,
                                        plan.L, w.head_dim, fixed, plan.tile_tokens)
     kv_bytes = kv_stream_bytes(sel_h.astype(np.int64), valid, plan.num_prefix_tiles, w.head_dim,
-                               bool(args.qk_fp8), fixed, plan.tile_tokens)
+                               bool(qk_fp8), fixed, plan.tile_tokens)
     coarse_flops = 4.0 * w.head_dim * plan.num_tiles ** 2 * w.heads
     total = alg_fine + coarse_flops
-    tflops = total / (ms_per_step * 1e-3) / 1e12
     fine_ms = float(stage[:, 2].mean())
-    fine_tflops = alg_fine / (fine_ms * 1e-3) / 1e12
-    # The fine branch runs as one launch per key chunk; the stage events span
-    # all of them, so per launch: the forward's flops and time over the count.
-    launches = max(plan.num_chunks, 1)
     # With FP8 q/k half of the fine flops (Q.K) run at the dense FP8 rate and
     # half (P.V) at the bf16 rate: the peak of that mix is their harmonic mean.
-    fine_peak = (2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS) if args.qk_fp8
+    fine_peak = (2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS) if qk_fp8
                  else PEAK_BF16_TFLOPS)
+    out_host = out.cpu()
+    r = {"x": x, "plan": plan, "out": out_host, "sel": sel_h, "ms": ms_per_step,
+         "event_ms": float(event_ms.mean()), "stage_ms": stage.mean(axis=0),
+         "alg_fine": alg_fine, "padded_fine": padded_fine, "kv_bytes": kv_bytes, "total": total,
+         "tflops": total / (ms_per_step * 1e-3) / 1e12, "fine_ms": fine_ms,
+         "fine_tflops": alg_fine / (fine_ms * 1e-3) / 1e12, "fine_peak": fine_peak,
+         "launches": max(plan.num_chunks, 1)}
+    del xd, ws, out, sel
+    plan.release_workspaces()
+    torch.cuda.empty_cache()
+    return r
+
+
+def stage_dict(st) -> dict:
+    return {"permute_pool": round(float(st[0]), 4), "coarse_topk": round(float(st[1]), 4),
+            "fine_attn": round(float(st[2]), 4)}
+
+
+def config_entry(w, r, with_parity=True) -> dict:
+    """One line of the ``configs`` array: time, throughput, fine-kernel
+    fraction of peak and head-0 parity for workload w."""
+    plan = r["plan"]
+    e = {"workload": w.name, "tokens": plan.L, "heads": w.heads, "head_dim": w.head_dim,
+         "prefix_tokens": w.n_prefix_tokens, "grid": list(w.grid), "sparsity": w.sparsity,
+         "topk": plan.topk, "tiles": plan.num_tiles, "tile": list(w.tile),
+         "ref_keep": w.ref_keep, "topk_ref": plan.topk_ref,
+         "ms_per_step": round(r["ms"], 4), "tflops_effective": round(r["tflops"], 2),
+         "pct_bf16_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+         "stage_ms": stage_dict(r["stage_ms"]),
+         "fine": {"achieved": round(r["fine_tflops"], 2), "peak": r["fine_peak"],
+                  "unit": "TFLOP/s", "frac": round(r["fine_tflops"] / r["fine_peak"], 4),
+                  "launches_per_forward": r["launches"], "key_chunk_tiles": plan.chunk_tiles}}
+    if with_parity:
+        g, hr, secs, _ = oracle_head(r["x"], w, 0)
+        _, parity = head_parity(g, hr, r["out"], r["sel"], 0)
+        e["parity"] = parity
+        e["oracle_head0_s"] = round(secs, 2)
+        log(f"bench: {w.name}: oracle head 0 {secs:.1f}s, parity {parity}")
+    return e
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="768p10s",
+                    help="a workload name from workloads.WORKLOADS, e.g. omniref768p10s "
+                         "(128-token tiles, reference keep 0.1)")
+    ap.add_argument("--configs", default=",".join(EXTRA_WORKLOADS),
+                    help="comma-separated workloads also timed (with head-0 parity against "
+                         "the oracle) and reported in the configs array; '' for none")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-tiles", type=int, default=0,
+                    help="key tiles per fine-branch key chunk (0: the library's default)")
+    ap.add_argument("--qk-fp8", action="store_true",
+                    help="time the forward with per-token FP8 (E4M3) q and k in the fine branch")
+    ap.add_argument("--qk-prep", action="store_true",
+                    help="time the forward with QK RMS norm + RoPE fused into the gather "
+                         "(synthetic weights and cos/sin tables)")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="counter runs: one 1 GiB device copy (traffic calibration), then the "
+                         "warmup and timed forwards; no CPU baseline, no other configs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the forward is single-GPU; multi-GPU sharding is a design note only)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, ROOT)
+    import video_dit_block_amd as vsa
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    log(f"bench: workload {w.name}: {w.description}")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    r = run_forward(w, args, torch, vsa, dev, args.qk_prep, args.qk_fp8, args.chunk_tiles,
+                    calibrate=args.profile_pass)
+    plan = r["plan"]
+    launches = r["launches"]
+    tflops = r["tflops"]
+    fine_ms = r["fine_ms"]
 
     metric = METRIC if w.name == "768p10s" else (
         f"VSA-H3 fwd ms and effective TFLOP/s (% bf16 MFMA peak) at {plan.L / 1000:.1f}k tokens")
@@ -330,7 +441,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -344,35 +455,44 @@ def main():
             "tile": list(w.tile), "ref_keep": w.ref_keep, "topk_ref": plan.topk_ref,
             "qk_prep": bool(args.qk_prep), "qk_fp8": bool(args.qk_fp8),
             "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-            "flops_effective": total, "flops_fine_padded_tiles": padded_fine,
-            "stage_ms": {"permute_pool": round(float(stage[:, 0].mean()), 4),
-                         "coarse_topk": round(float(stage[:, 1].mean()), 4),
-                         "fine_attn": round(fine_ms, 4)},
-            "event_ms_per_step": round(float(event_ms.mean()), 4),
+            "flops_effective": r["total"], "flops_fine_padded_tiles": r["padded_fine"],
+            "stage_ms": stage_dict(r["stage_ms"]),
+            "event_ms_per_step": round(r["event_ms"], 4),
         },
         "roofline": {
             "bound": "mfma", "kernel": "fine_attn_kernel",
-            "achieved": round(fine_tflops, 2), "peak": fine_peak, "unit": "TFLOP/s",
-            "frac": round(fine_tflops / fine_peak, 4),
+            "achieved": round(r["fine_tflops"], 2), "peak": r["fine_peak"], "unit": "TFLOP/s",
+            "frac": round(r["fine_tflops"] / r["fine_peak"], 4),
             "traffic": load_traffic(launches, w.name, plan.chunk_tiles),
             "launches_per_forward": launches,
             "key_chunk_tiles": plan.chunk_tiles,
-            "algorithmic_flops_per_launch": alg_fine / launches,
+            "algorithmic_flops_per_launch": r["alg_fine"] / launches,
             "avg_launch_ms": round(fine_ms / launches, 4),
             # The kernel's other ceiling: K/V bytes moved from L2 into LDS.
-            "kv_stream": {"bytes_per_launch": kv_bytes / launches,
-                          "achieved": round(kv_bytes / (fine_ms * 1e-3) / 1e12, 2),
+            "kv_stream": {"bytes_per_launch": r["kv_bytes"] / launches,
+                          "achieved": round(r["kv_bytes"] / (fine_ms * 1e-3) / 1e12, 2),
                           "unit": "TB/s"},
         },
     }
     if not args.no_cpu_baseline and not args.profile_pass and not args.qk_prep and not args.qk_fp8:
         log("bench: timing the CPU oracle on one head (bounded sample)")
-        cb, parity = cpu_baseline(x, w, out, sel_h, plan)
+        cb, parity = cpu_baseline(r["x"], w, r["out"], r["sel"])
         rec["cpu_baseline"] = cb
         rec["parity"] = parity
         log(f"bench: oracle head 0: {cb['seconds']:.1f}s, parity {parity}")
     else:
         rec["cpu_baseline"] = None
+    del r
+    extras = [n for n in args.configs.split(",") if n and n != w.name]
+    if args.profile_pass or args.qk_prep or args.qk_fp8:
+        extras = []
+    rec["configs"] = []
+    for name in extras:
+        we = WORKLOADS[name]
+        log(f"bench: config {we.name}: {we.description}")
+        re_ = run_forward(we, args, torch, vsa, dev)
+        rec["configs"].append(config_entry(we, re_, with_parity=not args.no_cpu_baseline))
+        del re_
     print(json.dumps(rec), flush=True)
 
 

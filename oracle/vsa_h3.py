@@ -144,6 +144,7 @@ pins above.
 from __future__ import annotations
 
 import math
+import time
 from dataclasses import dataclass
 
 import numpy as np
@@ -504,10 +505,20 @@ class HeadResult:
 
 def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
                  with_fine: bool = True, qk_fp8: bool = False,
-                 ref_keep: float = 1.0) -> HeadResult:
+                 ref_keep: float = 1.0, timings: dict | None = None) -> HeadResult:
     """The whole forward for head h.  q, k, v, gate: [L, H, D] (torch or numpy).
     qk_fp8: the fine branch uses per-token FP8 q and k (R19-R21).
-    ref_keep: reference keep ratio r of R23 (1 keeps every reference tile)."""
+    ref_keep: reference keep ratio r of R23 (1 keeps every reference tile).
+    timings: if a dict is given, the wall seconds of each step are added to
+    it under "pool", "scores", "topk", "coarse", "fine" and "combine"."""
+    clock = [time.perf_counter()]
+
+    def lap(name):
+        if timings is not None:
+            t = time.perf_counter()
+            timings[name] = timings.get(name, 0.0) + t - clock[0]
+            clock[0] = t
+
     qh = to_f32(q[:, h, :])
     kh = to_f32(k[:, h, :])
     vh = to_f32(v[:, h, :])
@@ -516,7 +527,9 @@ def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
     qp = pool_canonical(qh, geom)
     kp = pool_canonical(kh, geom)
     vp = pool_canonical(vh, geom)
+    lap("pool")
     S = scores_canonical(qp, kp)
+    lap("scores")
     sel = select_topk(S, geom, topk)
     ref_sel = None
     if not 0.0 < ref_keep <= 1.0:
@@ -524,7 +537,9 @@ def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
     if ref_keep < 1.0:
         ref_sel = select_ref(S, geom, ref_keep_count(int(np.sum(geom.tile_tag == COND)),
                                                      ref_keep))
+    lap("topk")
     c = coarse(S, vp, scale)
+    lap("coarse")
     o = out = None
     if with_fine:
         if qk_fp8:
@@ -533,7 +548,9 @@ def forward_head(q, k, v, gate, geom: Geometry, topk: int, h: int, items=None,
         else:
             q64, k64 = qh.astype(np.float64), kh.astype(np.float64)
         o = fine(q64, k64, vh.astype(np.float64), geom, sel, scale, items, ref_sel)
+        lap("fine")
         out = combine(o, to_f32(gate[:, h, :]), c, geom)
+        lap("combine")
     return HeadResult(qp, kp, vp, S, sel, c, o, out, ref_sel)
 
 

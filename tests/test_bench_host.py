@@ -130,3 +130,21 @@ def test_wide_fine_flops_and_kv_bytes_brute_force_over_blocks():
     # at head_dim 128 FP8 keys split over four waves too: once per query tile
     kv128 = kv[False] // kv_half[False] * (32 * 128 + 128 + 32 * 128 * 2)
     assert bench.kv_stream_bytes(sel, g.valid, g.P, 128, True, fixed, 128) == kv128
+
+
+def test_cpu_baseline_pieces_report_host_and_stage_split():
+    # host details: the logical CPU count as the OS reports it, a BLAS pool
+    hc = bench.host_cpu()
+    import os
+    assert hc["host_cpus"] == os.cpu_count()
+    assert hc["blas_threads"] is None or hc["blas_threads"] >= 1
+    # the oracle's stage split covers every step and adds up to the head's time
+    w, g = _geometry()
+    from workloads import make_inputs
+    x = make_inputs(w, seed=2)
+    g2, r, secs, stages = bench.oracle_head(x, w, 1)
+    assert set(stages) == {"pool", "scores", "topk", "coarse", "fine", "combine"}
+    assert 0.0 < sum(stages.values()) <= secs
+    ref = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g2,
+                              oracle.topk_count(g2.NV, w.sparsity), 1)
+    assert np.array_equal(r.out, ref.out) and np.array_equal(r.sel, ref.sel)
