@@ -79,7 +79,6 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
 
 template <typename T>
 struct IoOps;
@@ -406,6 +405,26 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   const char* vtl =
       SPLIT ? reinterpret_cast<const char*>(a.vt_lo) + static_cast<size_t>(hd) * Nb * V_TILE
             : nullptr;
+  // Buffer descriptors of this head's K, V^T (and low parts, key scales) for
+  // the DMA loads below: the MUBUF form takes a uniform byte offset in an
+  // SGPR and the lane's offset in one 32-bit VGPR, so no 64-bit address
+  // arithmetic runs per load, and the compiler's wait-count pass keeps exact
+  // LDS counts for the operand reads (it treats a global-segment load to LDS
+  // like a flat access and then waits for every outstanding LDS read).
+  // Word 3 selects 32-bit raw access (data format 32); reads past num_records
+  // return zero.
+  constexpr int kRawDword = 0x00020000;
+  const int kbytes = Nb * K_TILE, vbytes = Nb * V_TILE;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kth), 0, kbytes, kRawDword);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vth), 0, vbytes, kRawDword);
+  const __amdgpu_buffer_rsrc_t rkl =
+      KSPLIT ? __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ktl), 0, kbytes, kRawDword) : rk;
+  const __amdgpu_buffer_rsrc_t rvl =
+      SPLIT ? __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vtl), 0, vbytes, kRawDword) : rv;
+  const __amdgpu_buffer_rsrc_t rks =
+      QK8 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ksh), 0, Nb * 256, kRawDword) : rk;
   // Block of visit it.  Listed ids are clamped into [0, Nt): a corrupt list
   // can give a wrong result but never an out-of-bounds read.
   const int bmask = (1 << bsh) - 1;
@@ -445,29 +464,27 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 #define VSA_LOAD_KH(SLOT, J, B)                                                               \
   {                                                                                            \
     _Pragma("unroll") for (int p_ = 0; p_ < KPARTS; ++p_) {                                    \
-      const char* src_ = (p_ ? ktl : kth) + static_cast<size_t>(J) * K_TILE + (B) * KH_BYTES;  \
       _Pragma("unroll") for (int e = 0; e < KH_LOADS; ++e) {                                   \
         const int x_ = w * KH_LOADS + e;                                                       \
-        __builtin_amdgcn_global_load_lds(                                                      \
-            (gbl_void*)(src_ + kbase + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64),                \
-            (lds_void*)((SLOT) + p_ * KH_BYTES + x_ * 1024), 16, 0, 0);                        \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
+            p_ ? rkl : rk, (lds_void*)((SLOT) + p_ * KH_BYTES + x_ * 1024), 16, kbase,         \
+            (J) * K_TILE + (B) * KH_BYTES + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64, 0, 0);     \
       }                                                                                        \
     }                                                                                          \
     if (QK8 && w < 2)                                                                          \
-      __builtin_amdgcn_global_load_lds(                                                        \
-          (gbl_void*)(ksh + static_cast<size_t>(J) * 256 + 128 * (B) + 64 * w + 16 * (lane & 3)), \
-          (lds_void*)((SLOT) + KH_BYTES + 1024 * w), 16, 0, 0);                                \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_void*)((SLOT) + KH_BYTES + 1024 * w),  \
+                                               16, 16 * (lane & 3),                            \
+                                               (J) * 256 + 128 * (B) + 64 * w, 0, 0);          \
   }
 // Half B of V^T tile J into slot SLOT: VH_LOADS loads per wave and part.
 #define VSA_LOAD_VH(SLOT, J, B)                                                               \
   {                                                                                            \
     _Pragma("unroll") for (int p_ = 0; p_ < VPARTS; ++p_) {                                    \
-      const char* src_ = (p_ ? vtl : vth) + static_cast<size_t>(J) * V_TILE + (B) * VH_BYTES;  \
       _Pragma("unroll") for (int e = 0; e < VH_LOADS; ++e) {                                   \
         const int x_ = w * VH_LOADS + e;                                                       \
-        __builtin_amdgcn_global_load_lds((gbl_void*)(src_ + vbase + x_ * 1024),                \
-                                         (lds_void*)((SLOT) + p_ * VH_BYTES + x_ * 1024), 16,  \
-                                         0, 0);                                                \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
+            p_ ? rvl : rv, (lds_void*)((SLOT) + p_ * VH_BYTES + x_ * 1024), 16, vbase,         \
+            (J) * V_TILE + (B) * VH_BYTES + x_ * 1024, 0, 0);                                  \
       }                                                                                        \
     }                                                                                          \
   }
