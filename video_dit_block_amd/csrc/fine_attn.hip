@@ -30,7 +30,7 @@
 //     holds a token, so every row starts from a finite running max;
 //   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
 //     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
-//     global->LDS loads (global_load_lds_dwordx4, no register staging).  A
+//     global->LDS loads (buffer_load_dwordx4 ... lds, no register staging).  A
 //     slot is refilled with the next tile's half as soon as all waves have
 //     read it, so each load has about three quarters of an iteration to land
 //     (32 KB of LDS per workgroup: four two-wave or two four-wave
