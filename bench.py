@@ -359,6 +359,43 @@ def run_forward(w, args, torch, vsa, dev, qk_prep=False, qk_fp8=False, chunk_til
     return r
 
 
+def copy_tbps(torch, dev, reps=5) -> float:
+    """Read + write bandwidth of a 1 GiB device-to-device copy on this GPU,
+    in TB/s of bytes moved: the practical ceiling of a kernel whose traffic
+    mixes reads and writes, as the gather's does."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * n / (ms * 1e-3) / 1e12
+
+
+def gather_bytes(plan, w, qk_prep=False, qk_fp8=False) -> float:
+    """Algorithmic HBM bytes of the tile-permute gather with pooling: q, k, v
+    read once; K (bf16, or E4M3 codes and per-key scales) and V^T written per
+    64-slot block (pad slots included, they are stored zero), low parts with
+    fp32 I/O, Qt with QK-norm + RoPE; the pooled q, k, v tiles in fp32."""
+    es = 2 if w.io_dtype == "bf16" else 4
+    L, H, D, Nb, Nt = plan.L, w.heads, w.head_dim, plan.num_blocks, plan.num_tiles
+    parts = 1 if es == 2 else 2
+    blk = H * Nb * 64 * D
+    wr = blk * 2 * parts                                   # V^T
+    wr += blk * 1 + H * Nb * 64 * 4 if qk_fp8 else blk * 2 * parts   # K
+    if qk_prep:
+        wr += blk * 2 * parts                              # Qt
+    return 3.0 * L * H * D * es + wr + 3.0 * H * Nt * D * 4
+
+
 def stage_dict(st) -> dict:
     return {"permute_pool": round(float(st[0]), 4), "coarse_topk": round(float(st[1]), 4),
             "fine_attn": round(float(st[2]), 4)}
@@ -434,6 +471,10 @@ def main():
 
     metric = METRIC if w.name == "768p10s" else (
         f"VSA-H3 fwd ms and effective TFLOP/s (% bf16 MFMA peak) at {plan.L / 1000:.1f}k tokens")
+    # The gather's HBM traffic against a device copy's read + write rate.
+    gb = gather_bytes(plan, w, args.qk_prep, args.qk_fp8)
+    cp = copy_tbps(torch, dev)
+    g_tbps = gb / (float(r["stage_ms"][0]) * 1e-3) / 1e12
     rec = {
         "metric": metric,
         "value": round(tflops, 2),
@@ -458,6 +499,10 @@ def main():
             "flops_effective": r["total"], "flops_fine_padded_tiles": r["padded_fine"],
             "stage_ms": stage_dict(r["stage_ms"]),
             "event_ms_per_step": round(r["event_ms"], 4),
+            "permute_pool_hbm": {"bytes": gb, "achieved_tbps": round(g_tbps, 3),
+                                 "copy_tbps": round(cp, 3), "frac_of_copy": round(g_tbps / cp, 4),
+                                 "peak_tbps": PEAK_HBM_GBS / 1000.0,
+                                 "frac_of_peak": round(g_tbps / (PEAK_HBM_GBS / 1000.0), 4)},
         },
         "roofline": {
             "bound": "mfma", "kernel": "fine_attn_kernel",
