@@ -258,7 +258,7 @@ def cpu_baseline(x, w, gpu_out, gpu_sel, head=0):
           # the float64 fine branch (all but a few % of the time) is BLAS
           # matrix products; the other steps run on one thread
           "cores": hc["blas_threads"] or 1,
-          "kind": "oracle", "seconds": secs,
+          "kind": "oracle", "seconds": secs, "heads_timed": 1, "heads_total": w.heads,
           "sample": f"head {head} of {w.heads} of the {w.name} workload (whole per-head forward: "
                     "pool, scores, top-k, coarse, float64 fine branch, combine); value = that "
                     "head's effective flops over its wall time",
