@@ -476,23 +476,39 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
                                                16, 16 * (lane & 3),                            \
                                                (J) * 256 + 128 * (B) + 64 * w, 0, 0);          \
   }
-// Half B of V^T tile J into slot SLOT: VH_LOADS loads per wave and part.
+// Half B of V^T tile J into slot SLOT: VH_LOADS loads per wave and part.  A
+// V^T half is stored in LDS order, so this wave's loads cover consecutive
+// 1 KB of both memory and LDS: one LDS base (M0) and one SGPR offset serve
+// them all, and the instruction's immediate offset, which the hardware adds
+// to the global and to the LDS address alike, steps through them.
 #define VSA_LOAD_VH(SLOT, J, B)                                                               \
   {                                                                                            \
     _Pragma("unroll") for (int p_ = 0; p_ < VPARTS; ++p_) {                                    \
-      _Pragma("unroll") for (int e = 0; e < VH_LOADS; ++e) {                                   \
-        const int x_ = w * VH_LOADS + e;                                                       \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
-            p_ ? rvl : rv, (lds_void*)((SLOT) + p_ * VH_BYTES + x_ * 1024), 16, vbase,         \
-            (J) * V_TILE + (B) * VH_BYTES + x_ * 1024, 0, 0);                                  \
-      }                                                                                        \
+      char* const l_ = (SLOT) + p_ * VH_BYTES + w * VH_LOADS * 1024;                           \
+      const int s_ = (J) * V_TILE + (B) * VH_BYTES + w * VH_LOADS * 1024;                     \
+      VSA_VLOAD(0);                                                                            \
+      if (VH_LOADS > 1) VSA_VLOAD(1024);                                                       \
+      if (VH_LOADS > 2) VSA_VLOAD(2048);                                                       \
+      if (VH_LOADS > 3) VSA_VLOAD(3072);                                                       \
     }                                                                                          \
   }
+// (the immediate offset must be a literal)
+#define VSA_VLOAD(OFF)                                                                         \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rvl : rv, (lds_void*)l_, 16, vbase, s_, OFF, 0)
   // Loads this wave issues for half b of a tile with n valid keys.
   constexpr int CKMAX = KPARTS * KH_LOADS + (QK8 ? 1 : 0);
   const int CK = KPARTS * KH_LOADS + (QK8 && w < 2 ? 1 : 0);
   constexpr int CV = VPARTS * VH_LOADS;
   static_assert(2 * (CKMAX > CV ? CKMAX : CV) <= 16, "wait counts above 16");
+  static_assert(VH_LOADS * 1024 <= 4096, "immediate offsets of a V^T half fit in 12 bits");
+  // Every visited block holds a key (a tile's first block always does, and
+  // an empty second block of a 128-token tile is stepped over), so its first
+  // K and V^T halves are always loaded: each wait below has two possible
+  // counts, chosen by whether a second half was loaded.  They are
+  // compile-time constants unless the K load count differs between waves
+  // (FP8 keys with four waves: only waves 0 and 1 load the scales).
+  constexpr bool kStaticWaits = !QK8 || NW == 2;
+  constexpr int CKS = CKMAX;   // == CK for every wave when kStaticWaits
   auto ck = [CK](int n, int b) -> int { return n > 32 * b ? CK : 0; };
   auto cv = [](int n, int b) -> int { return n > 32 * b ? CV : 0; };
   // Wait until at most n of this wave's loads are in flight.
@@ -511,6 +527,15 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     }
   };
 
+  // Wait until at most A (if C) or B (else) of this wave's loads are in
+  // flight; A and B are compile-time constants.
+#define VSA_WAIT2(C, A, B)                                  \
+  do {                                                      \
+    if (C)                                                  \
+      __builtin_amdgcn_s_waitcnt(wait_vm_imm(A));           \
+    else                                                    \
+      __builtin_amdgcn_s_waitcnt(wait_vm_imm(B));           \
+  } while (0)
   // Swizzle of this lane's operand rows (key l32 of a K half, V^T row
   // 32n + l32; the latter does not depend on n).
   const int rswz = swz64(l32);
@@ -795,7 +820,10 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     }
 
     // K half 0 of t landed; every wave is done with V^T half 1 of t - 1.
-    wait_vm(ck(nj, 1) + cv(nj, 0));
+    if constexpr (kStaticWaits)
+      VSA_WAIT2(has1, CKS + CV, CV);
+    else
+      wait_vm(ck(nj, 1) + cv(nj, 0));
     VSA_BARRIER();
     if (has1) VSA_LOAD_VH(lds_vb, j, 1);
 
@@ -815,7 +843,10 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       }
     }
     // K half 1 of t landed; every wave is done with K half 0 of t.
-    wait_vm(cv(nj, 0) + cv(nj, 1));
+    if constexpr (kStaticWaits)
+      VSA_WAIT2(has1, 2 * CV, CV);
+    else
+      wait_vm(cv(nj, 0) + cv(nj, 1));
     VSA_BARRIER();
     VSA_LOAD_KH(lds_ka, jn, 0);
 
@@ -843,7 +874,10 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     const bool resc1 = __builtin_amdgcn_ballot_w64(alpha1 != 1.0f) != 0;
 
     // V^T half 0 of t landed; every wave is done with K half 1 of t.
-    wait_vm(cv(nj, 1) + ck(njn, 0));
+    if constexpr (kStaticWaits)
+      VSA_WAIT2(has1, CV + CKS, CKS);
+    else
+      wait_vm(cv(nj, 1) + ck(njn, 0));
     VSA_BARRIER();
     if (njn > 32) VSA_LOAD_KH(lds_kb, jn, 1);
 
@@ -873,7 +907,10 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       }
     }
     // V^T half 1 of t landed; every wave is done with V^T half 0 of t.
-    wait_vm(ck(njn, 0) + ck(njn, 1));
+    if constexpr (kStaticWaits)
+      VSA_WAIT2(njn > 32, 2 * CKS, CKS);
+    else
+      wait_vm(ck(njn, 0) + ck(njn, 1));
     VSA_BARRIER();
     VSA_LOAD_VH(lds_va, jn, 0);
 
@@ -890,6 +927,8 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 #undef VSA_LOAD_KH
 #undef VSA_LOAD_VH
 #undef VSA_BARRIER
+#undef VSA_WAIT2
+#undef VSA_VLOAD
 
   if (!last) {
     if (active) {
