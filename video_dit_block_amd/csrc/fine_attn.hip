@@ -447,6 +447,9 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   // for every load, the rest is uniform.
   const int lane_sw = ((lane & 3) ^ ((lane >> 4) & 3)) << 4;
   const int kbase = (lane >> 2) * KROWB + lane_sw;
+  // The same 16 rows further, less the 1 KB that the immediate offset adds.
+  const int kbase2 = kbase + 16 * KROWB - 1024;
+  static_assert(16 * KROWB >= 1024, "second lane offset is non-negative");
   const int vbase = (lane >> 2) * 64 + lane_sw;
 // Block barrier without the workgroup fence of __syncthreads(): the fence
 // would also wait for every outstanding global->LDS load, which this loop
@@ -461,14 +464,30 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 // lanes 0..3).
 // Pad rows are zero in memory, so a loaded half holds no stale data; a half
 // without valid keys is neither loaded nor read.
+// With an even number of loads per wave, loads x and x + 1 (x even) fill the
+// two 16-row halves of one 64-byte group: they share an LDS base and an SGPR
+// offset, the second adding 1 KB to both addresses through the immediate
+// offset and the rest of its 16-row step through a second lane offset.
 #define VSA_LOAD_KH(SLOT, J, B)                                                               \
   {                                                                                            \
     _Pragma("unroll") for (int p_ = 0; p_ < KPARTS; ++p_) {                                    \
-      _Pragma("unroll") for (int e = 0; e < KH_LOADS; ++e) {                                   \
-        const int x_ = w * KH_LOADS + e;                                                       \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
-            p_ ? rkl : rk, (lds_void*)((SLOT) + p_ * KH_BYTES + x_ * 1024), 16, kbase,         \
-            (J) * K_TILE + (B) * KH_BYTES + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64, 0, 0);     \
+      if constexpr (KH_LOADS % 2 == 0) {                                                       \
+        _Pragma("unroll") for (int e = 0; e < KH_LOADS; e += 2) {                              \
+          const int x_ = w * KH_LOADS + e;                                                     \
+          char* const l_ = (SLOT) + p_ * KH_BYTES + x_ * 1024;                                 \
+          const int s_ = (J) * K_TILE + (B) * KH_BYTES + (x_ >> 1) * 64;                       \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rkl : rk, (lds_void*)l_, 16, kbase, s_, \
+                                                   0, 0);                                      \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rkl : rk, (lds_void*)l_, 16, kbase2,   \
+                                                   s_, 1024, 0);                               \
+        }                                                                                      \
+      } else {                                                                                 \
+        _Pragma("unroll") for (int e = 0; e < KH_LOADS; ++e) {                                 \
+          const int x_ = w * KH_LOADS + e;                                                     \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(                                            \
+              p_ ? rkl : rk, (lds_void*)((SLOT) + p_ * KH_BYTES + x_ * 1024), 16, kbase,       \
+              (J) * K_TILE + (B) * KH_BYTES + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64, 0, 0);   \
+        }                                                                                      \
       }                                                                                        \
     }                                                                                          \
     if (QK8 && w < 2)                                                                          \
