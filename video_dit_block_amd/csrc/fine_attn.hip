@@ -37,9 +37,13 @@
 //     workgroups per CU);
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so
 //     each lane holds one query column), online softmax in fp32 via exp2 with
-//     the 1/sqrt(D) scale folded into log2 units; the running max is raised
-//     only when a tile exceeds it by more than 2^8 (probabilities stay below
-//     256, exact enough for bf16 P and fp32 sums), so the O rescale is rare;
+//     the 1/sqrt(D) scale folded into log2 units.  The exps of a half tile
+//     are taken against the running max as it stands, with no max pass: the
+//     max is raised, O and the row sum rescaled and the half redone only when
+//     a lane's sum of the half's probabilities is not in [0, 2^20] (always at
+//     a row's first block, whose running max is still -inf).  Probabilities
+//     then stay below 2^20, far inside fp32 and bf16 range, and the result
+//     differs from a max-subtracted softmax only by rounding;
 //   - O^T += V^T P^T on the same MFMA: P^T is consumed straight from the S^T
 //     accumulator layout; V^T is stored with the keys of each 16-key group
 //     permuted (0-3, 8-11, 4-7, 12-15) so that each lane's 8 keys are one
@@ -50,9 +54,8 @@
 //   - each key tile is taken in two 32-key halves, and the exp of one half
 //     is issued between the MFMAs of the other (Q.K of the second half, then
 //     P.V of the first), so softmax arithmetic and matrix work can overlap
-//     inside each wave; a half without valid keys is skipped, and the
-//     running max is tested per lane, with the row's two lanes combined only
-//     when it has to rise;
+//     inside each wave; a half without valid keys is skipped, and the row's
+//     two lanes are combined only when its running max has to rise;
 //   - blocks are mapped to the 8 XCDs so that each XCD works through its own
 //     heads, head by head: the 32 CUs of an XCD sweep the same head's K/V;
 //   - fp32 I/O keeps fp32-level accuracy on the bf16 matrix cores: every
@@ -704,30 +707,6 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       if constexpr (SPLIT) pwl[q] = pack_bf16x2_lo(p0, p1);
     }
   };
-  // p <- bf16(p * f) for the 8 probabilities of one operand.
-  auto rescale_bf16 = [](bf16x8& p, float f) {
-    u32x4 u = __builtin_bit_cast(u32x4, p);
-    u.x = pack_bf16x2(__uint_as_float(u.x << 16) * f, __uint_as_float(u.x & 0xffff0000u) * f);
-    u.y = pack_bf16x2(__uint_as_float(u.y << 16) * f, __uint_as_float(u.y & 0xffff0000u) * f);
-    u.z = pack_bf16x2(__uint_as_float(u.z << 16) * f, __uint_as_float(u.z & 0xffff0000u) * f);
-    u.w = pack_bf16x2(__uint_as_float(u.w << 16) * f, __uint_as_float(u.w & 0xffff0000u) * f);
-    p = __builtin_bit_cast(bf16x8, u);
-  };
-  // The same for a two-part (hi + lo) operand: the scaled sum is split again.
-  auto rescale_split = [](bf16x8& ph, bf16x8& pl, float f) {
-    u32x4 h = __builtin_bit_cast(u32x4, ph);
-    u32x4 l = __builtin_bit_cast(u32x4, pl);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = (__uint_as_float(h[e] << 16) + __uint_as_float(l[e] << 16)) * f;
-      const float x1 =
-          (__uint_as_float(h[e] & 0xffff0000u) + __uint_as_float(l[e] & 0xffff0000u)) * f;
-      h[e] = pack_bf16x2(x0, x1);
-      l[e] = pack_bf16x2_lo(x0, x1);
-    }
-    ph = __builtin_bit_cast(bf16x8, h);
-    pl = __builtin_bit_cast(bf16x8, l);
-  };
   auto pack16 = [](const uint32_t pw[8], bf16x8& pa, bf16x8& pb) {
     pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
     pb = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
@@ -796,14 +775,30 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[r]);
     return m;
   };
-  // New running max (log2 units) when some row of the wave has a score more
-  // than 2^8 above it, else m_run itself.  Each lane tests its own 16 keys
-  // of a row; only then are the two halves of each row (lanes l, l ^ 32)
-  // combined, so the common case needs no cross-lane exchange.
-  auto raised_max = [&](float mx_lane) -> float {
-    if (__builtin_amdgcn_ballot_w64(mx_lane * scale_log2 > m_run + 8.0f) == 0) return m_run;
-    const float mx = fmaxf(mx_lane, __shfl_xor(mx_lane, 32));
-    return fmaxf(m_run, mx * scale_log2);
+  // The exps of a half are taken against the running max as it stands; it
+  // is raised only when some lane's sum of the half's 16 probabilities
+  // leaves [0, 2^20] (a score far above it, or the row's first block, whose
+  // running max is still -inf: then the sum is inf or NaN).
+  auto overflowed = [&](float ps) -> bool {
+    return __builtin_amdgcn_ballot_w64(!(ps <= 1048576.0f)) != 0;
+  };
+  // Rare: raise the running max of each row to the half's maximum (the row's
+  // two lanes combined), move O and the row sum to it, and redo the half's
+  // probabilities and their sum.
+  auto redo_half = [&](const f32x16& s, float& ps, bf16x8& pa, bf16x8& pb, bf16x8& pal,
+                       bf16x8& pbl) {
+    const float mx = max16(s);
+    const float mnew = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+    m_run = mnew;
+    l_run *= alpha;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) oacc[n] *= alpha;
+    uint32_t pv[8], pvl[8];
+    ps = 0.0f;
+    sm_part(0, 1, s, m_run, pv, pvl, ps);
+    pack16(pv, pa, pb);
+    if constexpr (SPLIT) pack16(pvl, pal, pbl);
   };
 
   int j = 0, nj = 0;
@@ -852,14 +847,6 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       // Phase 1.
       qk_phase(0, s0, false, kNone, 0.0f, pf[0], pf[1], pfl[0], pfl[1]);
       if (nj < 32) mask_half(s0, 0, nj);
-      const float m0 = raised_max(max16(s0));
-      if (m0 != m_run) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m0);
-        m_run = m0;
-        l_run *= alpha;
-#pragma unroll
-        for (int n = 0; n < NB; ++n) oacc[n] *= alpha;
-      }
     }
     // K half 1 of t landed; every wave is done with K half 0 of t.
     if constexpr (kStaticWaits)
@@ -869,28 +856,23 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     VSA_BARRIER();
     VSA_LOAD_KH(lds_ka, jn, 0);
 
-    float alpha1 = 1.0f;
     if (active) {
-      // Phase 2 (the pinned copy keeps the softmax inside the branch).
+      // Phase 2: the exps of half 0 against the running max as it stands
+      // (the pinned copy keeps the softmax inside the branch).
+      float ps;
       if (has1) {
-        l_run += qk_phase(1, s1, true, s0, pinned(m_run), pf[0], pf[1], pfl[0], pfl[1]);
+        ps = qk_phase(1, s1, true, s0, pinned(m_run), pf[0], pf[1], pfl[0], pfl[1]);
       } else {
         uint32_t pv[8], pvl[8];
-        float ps = 0.0f;
+        ps = 0.0f;
         sm_part(0, 1, s0, m_run, pv, pvl, ps);
         pack16(pv, pf[0], pf[1]);
         if constexpr (SPLIT) pack16(pvl, pfl[0], pfl[1]);
-        l_run += ps;
       }
-      // The second half's max is settled before P.V of the first half starts.
-      if (has1) {
-        if (nj < 64) mask_half(s1, 1, nj);
-        const float m1 = raised_max(max16(s1));
-        alpha1 = __builtin_amdgcn_exp2f(m_run - m1);
-        m_run = m1;
-      }
+      if (overflowed(ps)) redo_half(s0, ps, pf[0], pf[1], pfl[0], pfl[1]);
+      l_run += ps;
+      if (has1 && nj < 64) mask_half(s1, 1, nj);
     }
-    const bool resc1 = __builtin_amdgcn_ballot_w64(alpha1 != 1.0f) != 0;
 
     // V^T half 0 of t landed; every wave is done with K half 1 of t.
     if constexpr (kStaticWaits)
@@ -902,24 +884,13 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 
     if (active) {
       if (has1) {
-        if (resc1) {
-          // Rare: the second half raised the max.  O, the row sum and the
-          // first half's probabilities (already bf16) move to the new max
-          // before they are combined, so O is only ever updated in place.
-          l_run *= alpha1;
-#pragma unroll
-          for (int n = 0; n < NB; ++n) oacc[n] *= alpha1;
-          if constexpr (SPLIT) {
-            rescale_split(pf[0], pfl[0], alpha1);
-            rescale_split(pf[1], pfl[1], alpha1);
-          } else {
-            rescale_bf16(pf[0], alpha1);
-            rescale_bf16(pf[1], alpha1);
-          }
-        }
         // Phase 3.
-        l_run += pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], true, s1, pinned(m_run), pf[2], pf[3],
-                          pfl[2], pfl[3]);
+        float ps = pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], true, s1, pinned(m_run), pf[2], pf[3],
+                            pfl[2], pfl[3]);
+        // O already holds P.V of half 0 at the running max, so a raise here
+        // rescales it with the row sum.
+        if (overflowed(ps)) redo_half(s1, ps, pf[2], pf[3], pfl[2], pfl[3]);
+        l_run += ps;
       } else {
         pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], false, kNone, 0.0f, pf[2], pf[3], pfl[2],
                  pfl[3]);
