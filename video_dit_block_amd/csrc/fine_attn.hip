@@ -30,10 +30,12 @@
 //     holds a token, so every row starts from a finite running max;
 //   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
 //     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
-//     global->LDS loads (buffer_load_dwordx4 ... lds, no register staging).  A
-//     slot is refilled with the next tile's half as soon as all waves have
-//     read it, so each load has about three quarters of an iteration to land
-//     (32 KB of LDS per workgroup: four two-wave or two four-wave
+//     global->LDS loads (buffer_load_dwordx4 ... lds, no register staging).
+//     The waves sync twice per tile: at the top, K of the tile has landed and
+//     the V^T slots take its V^T; after the two Q.K phases, V^T has landed
+//     and the K slots take the next tile's K.  Each load has two of the
+//     tile's four phases to land, and every wait is for all of the wave's
+//     loads (32 KB of LDS per workgroup: four two-wave or two four-wave
 //     workgroups per CU);
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so
 //     each lane holds one query column), online softmax in fp32 via exp2 with
@@ -184,13 +186,11 @@ __device__ __forceinline__ void decode_item_chunked(int b, int H, int n, int& h,
   }
 }
 
-// s_waitcnt immediate that waits for vmcnt <= N (N < 16, OR-ed in) and leaves
-// expcnt and lgkmcnt unconstrained.  The builtin, unlike inline asm, is seen
-// by the compiler's own wait-count pass, which then does not add a
-// conservative vmcnt(0) in front of the LDS reads.
+// s_waitcnt immediate that waits for vmcnt 0 and leaves expcnt and lgkmcnt
+// unconstrained.  The builtin, unlike inline asm, is seen by the compiler's
+// own wait-count pass, which then does not add a conservative vmcnt(0) in
+// front of the LDS reads.
 constexpr int kWaitVm = 0x0F70;
-// The same with vmcnt <= N for N < 64 (vmcnt bits 5:4 sit in bits 15:14).
-constexpr int wait_vm_imm(int n) { return kWaitVm | (n & 15) | ((n >> 4) << 14); }
 
 // XOR swizzle of the 16-byte chunk index inside a 64-byte LDS row: rows
 // r, r + 4, r + 8, r + 12 differ, so the 16 lanes of one pass of a 16-byte
@@ -454,11 +454,10 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   const int kbase2 = kbase + 16 * KROWB - 1024;
   static_assert(16 * KROWB >= 1024, "second lane offset is non-negative");
   const int vbase = (lane >> 2) * 64 + lane_sw;
-// Block barrier without the workgroup fence of __syncthreads(): the fence
-// would also wait for every outstanding global->LDS load, which this loop
-// keeps in flight on purpose.  LDS reads are drained first (so no wave's
-// pending read can race the next DMA into that region) and DMA completion is
-// awaited explicitly (kWaitVm) before the barriers that publish a slot.  The
+// Block barrier without the workgroup fence of __syncthreads() and its cache
+// maintenance.  LDS reads are drained first (so no wave's pending read can
+// race the next DMA into that region); DMA completion is awaited explicitly
+// (kWaitVm) right before each barrier, which then publishes the slots.  The
 // memory clobber keeps the compiler from moving memory accesses across it.
 #define VSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 // Half B of K tile J into slot SLOT: KH_LOADS loads per wave (per part: the
@@ -517,47 +516,7 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 // (the immediate offset must be a literal)
 #define VSA_VLOAD(OFF)                                                                         \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rvl : rv, (lds_void*)l_, 16, vbase, s_, OFF, 0)
-  // Loads this wave issues for half b of a tile with n valid keys.
-  constexpr int CKMAX = KPARTS * KH_LOADS + (QK8 ? 1 : 0);
-  const int CK = KPARTS * KH_LOADS + (QK8 && w < 2 ? 1 : 0);
-  constexpr int CV = VPARTS * VH_LOADS;
-  static_assert(2 * (CKMAX > CV ? CKMAX : CV) <= 16, "wait counts above 16");
   static_assert(VH_LOADS * 1024 <= 4096, "immediate offsets of a V^T half fit in 12 bits");
-  // Every visited block holds a key (a tile's first block always does, and
-  // an empty second block of a 128-token tile is stepped over), so its first
-  // K and V^T halves are always loaded: each wait below has two possible
-  // counts, chosen by whether a second half was loaded.  They are
-  // compile-time constants unless the K load count differs between waves
-  // (FP8 keys with four waves: only waves 0 and 1 load the scales).
-  constexpr bool kStaticWaits = !QK8 || NW == 2;
-  constexpr int CKS = CKMAX;   // == CK for every wave when kStaticWaits
-  auto ck = [CK](int n, int b) -> int { return n > 32 * b ? CK : 0; };
-  auto cv = [](int n, int b) -> int { return n > 32 * b ? CV : 0; };
-  // Wait until at most n of this wave's loads are in flight.
-  auto wait_vm = [](int n) {
-    switch (n) {
-#define VSA_WAIT_CASE(N) \
-  case N:                \
-    __builtin_amdgcn_s_waitcnt(wait_vm_imm(N)); \
-    break;
-      VSA_WAIT_CASE(1) VSA_WAIT_CASE(2) VSA_WAIT_CASE(3) VSA_WAIT_CASE(4) VSA_WAIT_CASE(5)
-      VSA_WAIT_CASE(6) VSA_WAIT_CASE(7) VSA_WAIT_CASE(8) VSA_WAIT_CASE(9) VSA_WAIT_CASE(10)
-      VSA_WAIT_CASE(11) VSA_WAIT_CASE(12) VSA_WAIT_CASE(13) VSA_WAIT_CASE(14)
-      VSA_WAIT_CASE(15) VSA_WAIT_CASE(16)
-#undef VSA_WAIT_CASE
-      default: __builtin_amdgcn_s_waitcnt(wait_vm_imm(0)); break;   // 0 (or, never, more)
-    }
-  };
-
-  // Wait until at most A (if C) or B (else) of this wave's loads are in
-  // flight; A and B are compile-time constants.
-#define VSA_WAIT2(C, A, B)                                  \
-  do {                                                      \
-    if (C)                                                  \
-      __builtin_amdgcn_s_waitcnt(wait_vm_imm(A));           \
-    else                                                    \
-      __builtin_amdgcn_s_waitcnt(wait_vm_imm(B));           \
-  } while (0)
   // Swizzle of this lane's operand rows (key l32 of a K half, V^T row
   // 32n + l32; the latter does not depend on n).
   const int rswz = swz64(l32);
@@ -807,21 +766,17 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     nj = valid[j];
     VSA_LOAD_KH(lds_ka, j, 0);
     if (nj > 32) VSA_LOAD_KH(lds_kb, j, 1);
-    VSA_LOAD_VH(lds_va, j, 0);
   }
-  // Query and state registers (and the first tile's halves) have landed.
-  __builtin_amdgcn_s_waitcnt(kWaitVm);
 
-  // Slot ring: each half tile is requested as soon as its slot has been read
-  // by all waves, about three quarters of an iteration before it is needed.
-  // Issue order, in iteration t: V^T half 1 of t, then K half 0, K half 1 and
-  // V^T half 0 of t + 1; each wait below counts the loads issued after the
-  // half it needs.
+  // Slot ring, two syncs per tile: at the top of iteration t, K of t has
+  // landed and every wave is done with V^T of t - 1, whose slots then take
+  // V^T of t; after phase 2, V^T of t has landed and every wave is done with
+  // K of t, whose slots then take K of t + 1.  Each load has two phases to
+  // land, and at each wait nothing else is in flight.
   const f32x16 kNone = {};
   for (int it = beg; it < end;) {
     const bool has1 = nj > 32;   // the second half holds a valid key
-    // The last iteration re-requests its own tile, so that every iteration
-    // issues the same loads and the wait counts stay exact.  A block without
+    // The last iteration re-requests its own tile's K.  A block without
     // valid keys (only ever the second block of a short 128-token tile) is
     // stepped over.
     int itn = it + 1;
@@ -833,12 +788,11 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       njn = valid[jn];
     }
 
-    // K half 0 of t landed; every wave is done with V^T half 1 of t - 1.
-    if constexpr (kStaticWaits)
-      VSA_WAIT2(has1, CKS + CV, CV);
-    else
-      wait_vm(ck(nj, 1) + cv(nj, 0));
+    // K of t landed (and, at the first tile, the query and state registers);
+    // every wave is done with V^T of t - 1.
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
     VSA_BARRIER();
+    VSA_LOAD_VH(lds_va, j, 0);
     if (has1) VSA_LOAD_VH(lds_vb, j, 1);
 
     f32x16 s0, s1;
@@ -847,16 +801,6 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       // Phase 1.
       qk_phase(0, s0, false, kNone, 0.0f, pf[0], pf[1], pfl[0], pfl[1]);
       if (nj < 32) mask_half(s0, 0, nj);
-    }
-    // K half 1 of t landed; every wave is done with K half 0 of t.
-    if constexpr (kStaticWaits)
-      VSA_WAIT2(has1, 2 * CV, CV);
-    else
-      wait_vm(cv(nj, 0) + cv(nj, 1));
-    VSA_BARRIER();
-    VSA_LOAD_KH(lds_ka, jn, 0);
-
-    if (active) {
       // Phase 2: the exps of half 0 against the running max as it stands
       // (the pinned copy keeps the softmax inside the branch).
       float ps;
@@ -874,12 +818,10 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       if (has1 && nj < 64) mask_half(s1, 1, nj);
     }
 
-    // V^T half 0 of t landed; every wave is done with K half 1 of t.
-    if constexpr (kStaticWaits)
-      VSA_WAIT2(has1, CV + CKS, CKS);
-    else
-      wait_vm(cv(nj, 1) + ck(njn, 0));
+    // V^T of t landed; every wave is done with K of t.
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
     VSA_BARRIER();
+    VSA_LOAD_KH(lds_ka, jn, 0);
     if (njn > 32) VSA_LOAD_KH(lds_kb, jn, 1);
 
     if (active) {
@@ -891,22 +833,12 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
         // rescales it with the row sum.
         if (overflowed(ps)) redo_half(s1, ps, pf[2], pf[3], pfl[2], pfl[3]);
         l_run += ps;
+        // Phase 4.
+        pv_phase(1, pf[2], pf[3], pfl[2], pfl[3], false, kNone, 0.0f, pf[2], pf[3], pfl[2], pfl[3]);
       } else {
         pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], false, kNone, 0.0f, pf[2], pf[3], pfl[2],
                  pfl[3]);
       }
-    }
-    // V^T half 1 of t landed; every wave is done with V^T half 0 of t.
-    if constexpr (kStaticWaits)
-      VSA_WAIT2(njn > 32, 2 * CKS, CKS);
-    else
-      wait_vm(ck(njn, 0) + ck(njn, 1));
-    VSA_BARRIER();
-    VSA_LOAD_VH(lds_va, jn, 0);
-
-    if (active && has1) {
-      // Phase 4.
-      pv_phase(1, pf[2], pf[3], pfl[2], pfl[3], false, kNone, 0.0f, pf[2], pf[3], pfl[2], pfl[3]);
     }
     j = jn;
     nj = njn;
@@ -917,7 +849,6 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 #undef VSA_LOAD_KH
 #undef VSA_LOAD_VH
 #undef VSA_BARRIER
-#undef VSA_WAIT2
 #undef VSA_VLOAD
 
   if (!last) {
