@@ -651,33 +651,36 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
       oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, g == 0 ? pa : pb, oacc[n], 0, 0, 0);
     }
   };
-  // Softmax pairs [8k/NS, 8(k+1)/NS) of one half: p = exp2(s*scale - mref),
-  // packed to bf16 pair by pair (word r/2 of the two 16-key operands); with
-  // fp32 I/O also the low parts.
-  auto sm_part = [&](int k, int ns, const f32x16& sacc, float mref, uint32_t pw[8],
-                     uint32_t pwl[8], float& ps) {
+  // Softmax of elements [e0, e1) of one half's S^T accumulator (16 per lane):
+  // p = exp2(s*scale - mref), added to the lane sum ps in element order and
+  // packed to bf16 pairs (word e/2 of pw; low parts in pwl with fp32 I/O).
+  // Element 0 starts the sum; an even element waits in `odd` for its pair
+  // (ranges start at even elements).
+  auto sm_elems = [&](int e0, int e1, const f32x16& sacc, float mref, uint32_t pw[8],
+                      uint32_t pwl[8], float& ps, float& odd) {
 #pragma unroll
-    for (int q = 8 * k / ns; q < 8 * (k + 1) / ns; ++q) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * q], scale_log2, -mref));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * q + 1], scale_log2, -mref));
-      ps += p0;
-      ps += p1;
-      pw[q] = pack_bf16x2(p0, p1);
-      if constexpr (SPLIT) pwl[q] = pack_bf16x2_lo(p0, p1);
+    for (int e = e0; e < e1; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -mref));
+      ps = e == 0 ? p : ps + p;
+      if (e & 1) {
+        pw[e >> 1] = pack_bf16x2(odd, p);
+        if constexpr (SPLIT) pwl[e >> 1] = pack_bf16x2_lo(odd, p);
+      } else {
+        odd = p;
+      }
     }
   };
+  // The two 16-key P^T operands of a half from its packed words.
   auto pack16 = [](const uint32_t pw[8], bf16x8& pa, bf16x8& pb) {
     pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
     pb = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
   };
-  // Q.K of half b; if SM, the softmax of the other half (s_other, reference
-  // mref) is spread over the steps, giving probabilities pa, pb (low parts
-  // pal, pbl with fp32 I/O).  Returns that softmax's lane sum.
-  auto qk_phase = [&](int b, f32x16& acc, bool sm, const f32x16& s_other, float mref,
-                      bf16x8& pa, bf16x8& pb, bf16x8& pal, bf16x8& pbl) -> float {
+  // Q.K of half b into acc; if SM, softmax elements [e0, e0 + 8) of s_other
+  // (reference mref) are spread over the steps.
+  auto qk_phase = [&](int b, f32x16& acc, bool sm, const f32x16& s_other, float mref, int e0,
+                      uint32_t pw[8], uint32_t pwl[8], float& ps) {
     QkOp kf[kQkSteps];
-    uint32_t pv[8], pvl[8];
-    float ps = 0.0f;
+    float odd = 0.0f;
 #pragma unroll
     for (int k = 0; k < kAhead && k < kQkSteps; ++k) kf[k] = qk_read(b, k);
     __builtin_amdgcn_sched_barrier(0);
@@ -685,25 +688,24 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     for (int k = 0; k < kQkSteps; ++k) {
       if (k + kAhead < kQkSteps) kf[k + kAhead] = qk_read(b, k + kAhead);
       qk_step(k, kf[k], acc);
-      if (sm) sm_part(k, kQkSteps, s_other, mref, pv, pvl, ps);
+      if (sm)
+        sm_elems(e0 + 8 * k / kQkSteps, e0 + 8 * (k + 1) / kQkSteps, s_other, mref, pw, pwl, ps,
+                 odd);
       __builtin_amdgcn_sched_barrier(0);
     }
     key_scales(b, acc);
-    if (sm) {
-      pack16(pv, pa, pb);
-      if constexpr (SPLIT) pack16(pvl, pal, pbl);
-    }
-    return ps;
   };
-  // P.V of half b (probabilities pa, pb; low parts pal, pbl); if SM, the
-  // softmax of s_other is spread over the steps, giving qa, qb (qal, qbl).
-  // Returns that softmax's lane sum.
-  auto pv_phase = [&](int b, const bf16x8& pa, const bf16x8& pb, const bf16x8& pal,
-                      const bf16x8& pbl, bool sm, const f32x16& s_other, float mref, bf16x8& qa,
-                      bf16x8& qb, bf16x8& qal, bf16x8& qbl) -> float {
+  // P.V of half b with the half's packed probabilities pw (low parts pwl);
+  // if SM, softmax elements [e0, e0 + 8) of s_other are spread over the steps
+  // into qw (qwl).
+  auto pv_phase = [&](int b, const uint32_t pw[8], const uint32_t pwl[8], bool sm,
+                      const f32x16& s_other, float mref, int e0, uint32_t qw[8], uint32_t qwl[8],
+                      float& ps) {
+    bf16x8 pa, pb, pal, pbl;
+    float odd = 0.0f;
+    pack16(pw, pa, pb);
+    if constexpr (SPLIT) pack16(pwl, pal, pbl);
     PvOp vf[kPvSteps];
-    uint32_t pv[8], pvl[8];
-    float ps = 0.0f;
 #pragma unroll
     for (int k = 0; k < kAhead; ++k) vf[k] = pv_read(b, k);
     __builtin_amdgcn_sched_barrier(0);
@@ -711,14 +713,18 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     for (int k = 0; k < kPvSteps; ++k) {
       if (k + kAhead < kPvSteps) vf[k + kAhead] = pv_read(b, k + kAhead);
       pv_step(k, vf[k], pa, pb, pal, pbl);
-      if (sm) sm_part(k, kPvSteps, s_other, mref, pv, pvl, ps);
+      if (sm)
+        sm_elems(e0 + 8 * k / kPvSteps, e0 + 8 * (k + 1) / kPvSteps, s_other, mref, qw, qwl, ps,
+                 odd);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (sm) {
-      pack16(pv, qa, qb);
-      if constexpr (SPLIT) pack16(pvl, qal, qbl);
-    }
-    return ps;
+  };
+  // Softmax elements [e0, e0 + 8) of s alone (a phase without matrix work).
+  auto sm_phase = [&](const f32x16& sacc, float mref, int e0, uint32_t pw[8], uint32_t pwl[8],
+                      float& ps) {
+    float odd = 0.0f;
+    sm_elems(e0, e0 + 8, sacc, mref, pw, pwl, ps, odd);
+    __builtin_amdgcn_sched_barrier(0);
   };
   // Pad keys (index >= nj) of half b to -inf: key 32b + 8(r/4) + 4hl + r%4
   // is a pad key iff its constant part reaches nj - 32b - 4hl.
@@ -744,8 +750,7 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   // Rare: raise the running max of each row to the half's maximum (the row's
   // two lanes combined), move O and the row sum to it, and redo the half's
   // probabilities and their sum.
-  auto redo_half = [&](const f32x16& s, float& ps, bf16x8& pa, bf16x8& pb, bf16x8& pal,
-                       bf16x8& pbl) {
+  auto redo_half = [&](const f32x16& s, float& ps, uint32_t pw[8], uint32_t pwl[8]) {
     const float mx = max16(s);
     const float mnew = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
@@ -753,11 +758,8 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     l_run *= alpha;
 #pragma unroll
     for (int n = 0; n < NB; ++n) oacc[n] *= alpha;
-    uint32_t pv[8], pvl[8];
-    ps = 0.0f;
-    sm_part(0, 1, s, m_run, pv, pvl, ps);
-    pack16(pv, pa, pb);
-    if constexpr (SPLIT) pack16(pvl, pal, pbl);
+    float odd = 0.0f;
+    sm_elems(0, 16, s, m_run, pw, pwl, ps, odd);
   };
 
   int j = 0, nj = 0;
@@ -766,79 +768,98 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     nj = valid[j];
     VSA_LOAD_KH(lds_ka, j, 0);
     if (nj > 32) VSA_LOAD_KH(lds_kb, j, 1);
+    VSA_LOAD_VH(lds_va, j, 0);
   }
 
-  // Slot ring, two syncs per tile: at the top of iteration t, K of t has
-  // landed and every wave is done with V^T of t - 1, whose slots then take
-  // V^T of t; after phase 2, V^T of t has landed and every wave is done with
-  // K of t, whose slots then take K of t + 1.  Each load has two phases to
-  // land, and at each wait nothing else is in flight.
-  const f32x16 kNone = {};
-  for (int it = beg; it < end;) {
-    const bool has1 = nj > 32;   // the second half holds a valid key
-    // The last iteration re-requests its own tile's K.  A block without
-    // valid keys (only ever the second block of a short 128-token tile) is
-    // stepped over.
+  // The softmax of each half tile is split in two parts of 8 elements, and
+  // the work of tile t runs as four phases of matrix steps, each with one
+  // softmax part spread over its steps:
+  //   1. Q.K of half 0 of t        | second part of half 1 of t - 1;
+  //   2. P.V of half 1 of t - 1    | first part of half 0 of t;
+  //   3. Q.K of half 1 of t        | second part of half 0 of t;
+  //   4. P.V of half 0 of t        | first part of half 1 of t.
+  // A half's running-max check follows its second part, before its P.V, so
+  // the softmax, the P.V order and every rounding are those of a tile taken
+  // whole.  An extra iteration after the last tile finishes the last half 1.
+  // Slots, two syncs per tile: after phase 2 (A) every wave is done with
+  // K half 0 of t and V^T half 1 of t - 1, whose slots take K half 0 of t + 1
+  // and V^T half 1 of t; after phase 4 (B) every wave is done with K half 1
+  // and V^T half 0 of t, whose slots take those of t + 1.  At each sync the
+  // loads issued at the previous one have landed (two or three phases to
+  // land), and nothing else is in flight.
+  uint32_t w0[8], w0l[8], w1[8], w1l[8];   // packed probabilities of halves 0 and 1
+  float ps0 = 0.0f, ps1 = 0.0f;
+  // S^T of the halves.  The phases take a softmax part whether or not its
+  // half exists, so that the common path has no branches; a part taken of
+  // a half that does not exist (s1 of a tile whose second half holds no key)
+  // is never used.
+  f32x16 s0 = {}, s1 = {};
+  bool prev1 = false;   // half 1 of the previous tile awaits its second part and P.V
+  // K half 0 and 1 and V^T half 0 of the first tile landed (and the query
+  // and state registers).
+  __builtin_amdgcn_s_waitcnt(kWaitVm);
+  VSA_BARRIER();
+  for (int it = beg;;) {
+    const bool cur = it < end;
+    const bool has1 = cur && nj > 32;   // the second half holds a valid key
+    // The next visit (none after the last).  A block without valid keys
+    // (only ever the second block of a short 128-token tile) is stepped over.
     int itn = it + 1;
-    int jn = itn < end ? tile_at(itn) : j;
-    int njn = valid[jn];
-    if (bsh > 0 && njn == 0) {
-      ++itn;
-      jn = itn < end ? tile_at(itn) : j;
+    int jn = j, njn = 0;
+    if (itn < end) {
+      jn = tile_at(itn);
       njn = valid[jn];
+      if (bsh > 0 && njn == 0) {
+        ++itn;
+        jn = itn < end ? tile_at(itn) : j;
+        njn = itn < end ? valid[jn] : 0;
+      }
     }
-
-    // K of t landed (and, at the first tile, the query and state registers);
-    // every wave is done with V^T of t - 1.
-    __builtin_amdgcn_s_waitcnt(kWaitVm);
-    VSA_BARRIER();
-    VSA_LOAD_VH(lds_va, j, 0);
-    if (has1) VSA_LOAD_VH(lds_vb, j, 1);
-
-    f32x16 s0, s1;
-    bf16x8 pf[4], pfl[4];   // probabilities; low parts with fp32 I/O
     if (active) {
       // Phase 1.
-      qk_phase(0, s0, false, kNone, 0.0f, pf[0], pf[1], pfl[0], pfl[1]);
-      if (nj < 32) mask_half(s0, 0, nj);
-      // Phase 2: the exps of half 0 against the running max as it stands
-      // (the pinned copy keeps the softmax inside the branch).
-      float ps;
-      if (has1) {
-        ps = qk_phase(1, s1, true, s0, pinned(m_run), pf[0], pf[1], pfl[0], pfl[1]);
-      } else {
-        uint32_t pv[8], pvl[8];
-        ps = 0.0f;
-        sm_part(0, 1, s0, m_run, pv, pvl, ps);
-        pack16(pv, pf[0], pf[1]);
-        if constexpr (SPLIT) pack16(pvl, pfl[0], pfl[1]);
+      if (cur)
+        qk_phase(0, s0, true, s1, pinned(m_run), 8, w1, w1l, ps1);
+      else
+        sm_phase(s1, m_run, 8, w1, w1l, ps1);
+      if (prev1) {
+        if (overflowed(ps1)) redo_half(s1, ps1, w1, w1l);
+        l_run += ps1;
       }
-      if (overflowed(ps)) redo_half(s0, ps, pf[0], pf[1], pfl[0], pfl[1]);
-      l_run += ps;
-      if (has1 && nj < 64) mask_half(s1, 1, nj);
+      if (cur && nj < 32) mask_half(s0, 0, nj);
+      // Phase 2.
+      if (prev1)
+        pv_phase(1, w1, w1l, true, s0, pinned(m_run), 0, w0, w0l, ps0);
+      else
+        sm_phase(s0, m_run, 0, w0, w0l, ps0);
     }
+    if (!cur) break;
 
-    // V^T of t landed; every wave is done with K of t.
+    // Sync A: K half 1 and V^T half 0 of t landed.
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     VSA_BARRIER();
-    VSA_LOAD_KH(lds_ka, jn, 0);
-    if (njn > 32) VSA_LOAD_KH(lds_kb, jn, 1);
+    if (itn < end) VSA_LOAD_KH(lds_ka, jn, 0);
+    if (has1) VSA_LOAD_VH(lds_vb, j, 1);
 
     if (active) {
-      if (has1) {
-        // Phase 3.
-        float ps = pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], true, s1, pinned(m_run), pf[2], pf[3],
-                            pfl[2], pfl[3]);
-        // O already holds P.V of half 0 at the running max, so a raise here
-        // rescales it with the row sum.
-        if (overflowed(ps)) redo_half(s1, ps, pf[2], pf[3], pfl[2], pfl[3]);
-        l_run += ps;
-        // Phase 4.
-        pv_phase(1, pf[2], pf[3], pfl[2], pfl[3], false, kNone, 0.0f, pf[2], pf[3], pfl[2], pfl[3]);
-      } else {
-        pv_phase(0, pf[0], pf[1], pfl[0], pfl[1], false, kNone, 0.0f, pf[2], pf[3], pfl[2],
-                 pfl[3]);
-      }
+      // Phase 3.
+      if (has1)
+        qk_phase(1, s1, true, s0, pinned(m_run), 8, w0, w0l, ps0);
+      else
+        sm_phase(s0, m_run, 8, w0, w0l, ps0);
+      if (overflowed(ps0)) redo_half(s0, ps0, w0, w0l);
+      l_run += ps0;
+      if (has1 && nj < 64) mask_half(s1, 1, nj);
+      // Phase 4.
+      pv_phase(0, w0, w0l, true, s1, pinned(m_run), 0, w1, w1l, ps1);
+    }
+    prev1 = has1;
+
+    // Sync B: K half 0 of t + 1 and V^T half 1 of t landed.
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
+    VSA_BARRIER();
+    if (itn < end) {
+      if (njn > 32) VSA_LOAD_KH(lds_kb, jn, 1);
+      VSA_LOAD_VH(lds_va, jn, 0);
     }
     j = jn;
     nj = njn;
