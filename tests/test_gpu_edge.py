@@ -1,7 +1,9 @@
 """GPU edge cases through the C ABI against the CPU oracle: the largest plan
 the kernels take (4,096 tiles per head), logits large enough to move the
-running maximum often, exact score ties (the lower tile index wins), and a
-one-token video."""
+running maximum often, exact score ties (the lower tile index wins), a
+one-token video, and query tiles of at most 32 tokens (one of the query
+item's two waves then holds only pad rows), also where no key tile has more
+than 32 keys."""
 import math
 
 import numpy as np
@@ -9,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import video_dit_block_amd as vsa
 from tests.gpu_helpers import (F32_MAX_ABS, F32_REL_L2, assert_close, intermediates, out_f64,
                                require_gpu, run, say)
 from workloads import TEXT, Workload, make_inputs
@@ -114,6 +117,42 @@ def test_one_token_video():
                          w.grid, w.sparsity)
     assert np.array_equal(sel.cpu().numpy()[:, :, 0], np.full((2, 1), 1))
     assert_close(out_f64(out), ref["out"], "one-token video")
+
+
+SHORT_CASES = [
+    # every tile holds 32 tokens: no key tile has a second half
+    (Workload("short_all32", 4, 128, "bf16", (), (2, 8, 12), 0.5), 2),
+    (Workload("short_all32_f32", 2, 64, "f32", (), (2, 8, 12), 0.5), 3),
+    # a text prefix plus a last tile row of 2 frames: 32-token query tiles
+    # meet key tiles of 64 and of 32 tokens
+    (Workload("short_mixed", 4, 128, "bf16", ((TEXT, 64),), (6, 8, 12), 0.6), 4),
+    # a last tile row of 1 frame: 16-token query tiles, pad keys in the first half
+    (Workload("short_16", 2, 128, "bf16", ((TEXT, 40),), (5, 8, 8), 0.5), 3),
+]
+
+
+@pytest.mark.parametrize("w,ch", SHORT_CASES, ids=[c[0].name for c in SHORT_CASES])
+def test_query_tiles_of_at_most_32_tokens(w, ch):
+    say(f"case {w.name}: grid={w.grid} {w.io_dtype}, and chunk_tiles={ch}")
+    x = make_inputs(w, seed=12, video_order="shuffled")
+    out, sel, plan, ws = run(x, w.grid, w.sparsity)
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["gate"], x["token_tags"], x["position_ids"],
+                         w.grid, w.sparsity)
+    g = ref["geom"]
+    assert any(len(t) <= 32 for t in g.tiles[g.P:])
+    for h in range(w.heads):
+        assert np.array_equal(sel[h].cpu().numpy(), ref["heads"][h].sel), h
+    if w.io_dtype == "bf16":
+        assert_close(out_f64(out), ref["out"], w.name)
+    else:
+        assert_close(out_f64(out), ref["out"], w.name, F32_MAX_ABS, F32_REL_L2)
+    # key chunks pass the running state on bit for bit
+    chunked = vsa.Plan(x["token_tags"], x["position_ids"], w.grid, w.heads, w.head_dim,
+                       w.sparsity, chunk_tiles=ch, io_dtype=x["q"].dtype)
+    assert chunked.num_chunks > 1
+    out2, sel2, _, _ = run(x, w.grid, w.sparsity, plan=chunked)
+    assert torch.equal(sel2, sel)
+    assert torch.equal(out2, out)
 
 
 def _crafted_scores_inputs(values_per_head, seed):
