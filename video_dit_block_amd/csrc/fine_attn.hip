@@ -27,7 +27,10 @@
 //     then the selected video tiles) and visits each tile's blocks in order,
 //     stepping over a block without valid keys (the second block of a
 //     128-token tile with at most 64 tokens); a tile's first block always
-//     holds a token, so every row starts from a finite running max;
+//     holds a token, so every row starts from a finite running max; with
+//     64-token tiles, two consecutive visited tiles of at most 32 tokens (a
+//     short tile holds one half) are taken as the two halves of one
+//     iteration, in the same order;
 //   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
 //     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
 //     global->LDS loads (buffer_load_dwordx4 ... lds, no register staging).
@@ -185,6 +188,13 @@ __device__ __forceinline__ void decode_item_chunked(int b, int H, int n, int& h,
     i = b - h * n;
   }
 }
+
+// The key halves of one iteration of the fine kernel's loop.
+struct Visit {
+  int j, n0;        // block of the first half and its valid keys (1..32)
+  int j1, b1, n1;   // block and half of the second half, its valid keys (0..32)
+  int step;         // visits taken
+};
 
 // s_waitcnt immediate that waits for vmcnt 0 and leaves expcnt and lgkmcnt
 // unconstrained.  The builtin, unlike inline asm, is seen by the compiler's
@@ -726,8 +736,8 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     sm_elems(e0, e0 + 8, sacc, mref, pw, pwl, ps, odd);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Pad keys (index >= nj) of half b to -inf: key 32b + 8(r/4) + 4hl + r%4
-  // is a pad key iff its constant part reaches nj - 32b - 4hl.
+  // Pad keys (index >= n) of half b to -inf: key 32b + 8(r/4) + 4hl + r%4
+  // is a pad key iff its constant part reaches n - 32b - 4hl.
   auto mask_half = [&](f32x16& acc, int b, int n) {
     const int lim = n - 32 * b - 4 * hl;
 #pragma unroll
@@ -762,13 +772,40 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     sm_elems(0, 16, s, m_run, pw, pwl, ps, odd);
   };
 
-  int j = 0, nj = 0;
+  // An iteration takes one key block as two 32-key halves, or two
+  // consecutive visited blocks of at most 32 keys each (a short tile holds
+  // one half) as the two halves of one: the first half is always block j's
+  // keys 0-31, the second is block j's keys 32-63 or block j2's keys 0-31.
+  // The visit order, and so every operation on the running state, is the
+  // same either way.  `step` is the number of visits the iteration takes.
+  // With 128-token tiles no blocks are paired.
+  auto visit_at = [&](int at) -> Visit {
+    Visit v;
+    v.j = tile_at(at);
+    const int n = valid[v.j];
+    v.n0 = min(n, 32);
+    v.j1 = v.j;
+    v.b1 = 1;
+    v.n1 = max(n - 32, 0);
+    v.step = 1;
+    if (bsh == 0 && n <= 32 && at + 1 < end) {
+      const int j2 = tile_at(at + 1);
+      const int n2 = valid[j2];
+      if (n2 <= 32) {
+        v.j1 = j2;
+        v.b1 = 0;
+        v.n1 = n2;
+        v.step = 2;
+      }
+    }
+    return v;
+  };
+  Visit cv{};
   if (beg < end) {
-    j = tile_at(beg);
-    nj = valid[j];
-    VSA_LOAD_KH(lds_ka, j, 0);
-    if (nj > 32) VSA_LOAD_KH(lds_kb, j, 1);
-    VSA_LOAD_VH(lds_va, j, 0);
+    cv = visit_at(beg);
+    VSA_LOAD_KH(lds_ka, cv.j, 0);
+    if (cv.n1 > 0) VSA_LOAD_KH(lds_kb, cv.j1, cv.b1);
+    VSA_LOAD_VH(lds_va, cv.j, 0);
   }
 
   // The softmax of each half tile is split in two parts of 8 elements, and
@@ -801,18 +838,22 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   VSA_BARRIER();
   for (int it = beg;;) {
     const bool cur = it < end;
-    const bool has1 = cur && nj > 32;   // the second half holds a valid key
-    // The next visit (none after the last).  A block without valid keys
+    const bool has1 = cur && cv.n1 > 0;   // the second half holds a valid key
+    // The next iteration (none after the last).  A block without valid keys
     // (only ever the second block of a short 128-token tile) is stepped over.
-    int itn = it + 1;
-    int jn = j, njn = 0;
+    int itn = it + cv.step;
+    Visit nv = cv;
+    nv.n1 = 0;
     if (itn < end) {
-      jn = tile_at(itn);
-      njn = valid[jn];
-      if (bsh > 0 && njn == 0) {
+      nv = visit_at(itn);
+      if (bsh > 0 && nv.n0 == 0) {
         ++itn;
-        jn = itn < end ? tile_at(itn) : j;
-        njn = itn < end ? valid[jn] : 0;
+        if (itn < end) {
+          nv = visit_at(itn);
+        } else {
+          nv = cv;
+          nv.n1 = 0;
+        }
       }
     }
     if (active) {
@@ -825,7 +866,7 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
         if (overflowed(ps1)) redo_half(s1, ps1, w1, w1l);
         l_run += ps1;
       }
-      if (cur && nj < 32) mask_half(s0, 0, nj);
+      if (cur && cv.n0 < 32) mask_half(s0, 0, cv.n0);
       // Phase 2.
       if (prev1)
         pv_phase(1, w1, w1l, true, s0, pinned(m_run), 0, w0, w0l, ps0);
@@ -837,8 +878,8 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     // Sync A: K half 1 and V^T half 0 of t landed.
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     VSA_BARRIER();
-    if (itn < end) VSA_LOAD_KH(lds_ka, jn, 0);
-    if (has1) VSA_LOAD_VH(lds_vb, j, 1);
+    if (itn < end) VSA_LOAD_KH(lds_ka, nv.j, 0);
+    if (has1) VSA_LOAD_VH(lds_vb, cv.j1, cv.b1);
 
     if (active) {
       // Phase 3.
@@ -848,7 +889,7 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
         sm_phase(s0, m_run, 8, w0, w0l, ps0);
       if (overflowed(ps0)) redo_half(s0, ps0, w0, w0l);
       l_run += ps0;
-      if (has1 && nj < 64) mask_half(s1, 1, nj);
+      if (has1 && cv.n1 < 32) mask_half(s1, 1, 32 + cv.n1);
       // Phase 4.
       pv_phase(0, w0, w0l, true, s1, pinned(m_run), 0, w1, w1l, ps1);
     }
@@ -858,11 +899,10 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     VSA_BARRIER();
     if (itn < end) {
-      if (njn > 32) VSA_LOAD_KH(lds_kb, jn, 1);
-      VSA_LOAD_VH(lds_va, jn, 0);
+      if (nv.n1 > 0) VSA_LOAD_KH(lds_kb, nv.j1, nv.b1);
+      VSA_LOAD_VH(lds_va, nv.j, 0);
     }
-    j = jn;
-    nj = njn;
+    cv = nv;
     it = itn;
   }
   // No global->LDS load may still be in flight when the block's LDS is released.
