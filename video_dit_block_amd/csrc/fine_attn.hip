@@ -201,6 +201,9 @@ struct Visit {
 // own wait-count pass, which then does not add a conservative vmcnt(0) in
 // front of the LDS reads.
 constexpr int kWaitVm = 0x0F70;
+// The same, waiting until at most n vector-memory loads are outstanding
+// (vmcnt in bits 3:0 and 15:14).
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // XOR swizzle of the 16-byte chunk index inside a 64-byte LDS row: rows
 // r, r + 4, r + 8, r + 12 differ, so the 16 lanes of one pass of a 16-byte
@@ -260,6 +263,7 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   constexpr int NK64 = D / 64;                   // FP8 MFMA steps of 64 channels
   constexpr int NCK = D / 16;                    // QK contraction steps
   constexpr int NB = D / 32;                     // O^T blocks of 32 channels
+  constexpr int kWaitVmO = wait_vm(4 * NB);      // all but the 4 NB loads of O
   // Four LDS slots, one per half tile: K keys 0-31, K keys 32-63, V^T keys
   // 0-31 and V^T keys 32-63.  With QK8 a K slot is followed by 1 KB per wave
   // for per-key scales (the first 64 bytes hold the wave's 16 scales).
@@ -547,25 +551,13 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   float l_run = 0.0f;
   f32x4* wstate = reinterpret_cast<f32x4*>(state) +
                   ((static_cast<size_t>(hd) * Nb + ib) * 2 + w) * (4 * NB + 1) * 64 + lane;
-  if (!first && active) {
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const f32x4 t = __builtin_nontemporal_load(wstate + (4 * n + k4) * 64);
-        oacc[n][4 * k4 + 0] = t.x;
-        oacc[n][4 * k4 + 1] = t.y;
-        oacc[n][4 * k4 + 2] = t.z;
-        oacc[n][4 * k4 + 3] = t.w;
-      }
+  // The running max and sums come first; O follows the first tile's loads
+  // (below), since the first iteration needs it only from its last phase.
+  const bool load_state = !first && active;
+  if (load_state) {
     const f32x4 ml = __builtin_nontemporal_load(wstate + 4 * NB * 64);
     m_run = ml.x;
     l_run = ml.y;
-  } else {
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
   }
 
   // A key tile is taken in two halves of 32 keys; each half is 8 Q.K MFMA
@@ -832,9 +824,30 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   // is never used.
   f32x16 s0 = {}, s1 = {};
   bool prev1 = false;   // half 1 of the previous tile awaits its second part and P.V
+  if (load_state) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const f32x4 t = __builtin_nontemporal_load(wstate + (4 * n + k4) * 64);
+        oacc[n][4 * k4 + 0] = t.x;
+        oacc[n][4 * k4 + 1] = t.y;
+        oacc[n][4 * k4 + 2] = t.z;
+        oacc[n][4 * k4 + 3] = t.w;
+      }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
+  }
   // K half 0 and 1 and V^T half 0 of the first tile landed (and the query
-  // and state registers).
-  __builtin_amdgcn_s_waitcnt(kWaitVm);
+  // and the running max and sums); the 4 NB loads of O may still be in
+  // flight (the compiler waits for them where O is first used).
+  if (load_state)
+    __builtin_amdgcn_s_waitcnt(kWaitVmO);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
   VSA_BARRIER();
   for (int it = beg;;) {
     const bool cur = it < end;
