@@ -95,7 +95,9 @@ typedef struct {
 typedef struct {
   uint64_t perm;    /* int32 [Nb][64]: packed row of each slot, -1 for pad slots */
   uint64_t valid;   /* int32 [Nb]: valid tokens per block */
-  uint64_t kt;      /* bf16 [H][Nb][64][D]: keys in tile order, pad rows zero */
+  uint64_t kt;      /* bf16 [H][Nb][2][D/32][32][32]: keys in tile order, pad rows zero; per
+                       block, each half of 32 slots (0-31, 32-63) is stored group by group,
+                       a group holding 32 channels (64 bytes) of its 32 key rows */
   uint64_t vt;      /* bf16 [H][Nb][2][D][32]: values in tile order, transposed, in two halves
                        of 32 slots (0-31, 32-63) per block, pad columns zero; inside each
                        16-slot group the columns hold slots 0-3, 8-11, 4-7, 12-15 */
@@ -116,7 +118,8 @@ typedef struct {
                        internal layout */
   uint64_t qt;      /* bf16 [H][Nb][64][D]: q after QK-norm + RoPE, tile order, pad rows zero
                        (only with vsa_h3_plan_set_qk_prep) */
-  uint64_t kt8;     /* uint8 [H][Nb][64][D]: keys as OCP E4M3 codes, tile order, pad rows zero
+  uint64_t kt8;     /* uint8 [H][Nb][2][D/64][32][64]: keys as OCP E4M3 codes, tile order, pad
+                       rows zero, in the half and group order of kt (a group holds 64 codes)
                        (only with vsa_h3_plan_set_qk_fp8) */
   uint64_t kscale;  /* fp32 [H][Nb][64]: per-key dequantisation scale amax/448, pad slots zero
                        (only with vsa_h3_plan_set_qk_fp8) */

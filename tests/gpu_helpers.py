@@ -76,8 +76,19 @@ def oracle_prep(x, prep):
                           prep["eps"], prep["cos"].numpy(), prep["sin"].numpy())
 
 
+def key_rows(region: torch.Tensor, D: int, group: int) -> torch.Tensor:
+    """Key blocks [H][Nb][64][D] from the Kt layout (also that of Kt_lo and the
+    FP8 codes Kt8): per 64-slot block, each 32-slot half is stored as
+    [D / group][32 slots][group], group elements being 64 bytes of a row (32
+    bf16 channels or 64 FP8 codes).  region: the raw region as [H][Nb][64 * D]."""
+    H, Nb = region.shape[0], region.shape[1]
+    g = region.reshape(H, Nb, 2, D // group, 32, group)
+    return g.permute(0, 1, 2, 4, 3, 5).reshape(H, Nb, 64, D)
+
+
 def intermediates(plan, ws):
-    """Workspace regions on the host; kt and vt are per 64-slot block."""
+    """Workspace regions on the host; kt and vt are per 64-slot block (kt
+    returned as rows [H][Nb][64][D])."""
     H, D, Nt, Nb = plan.heads, plan.head_dim, plan.num_tiles, plan.num_blocks
     ns = plan.layout.scores_row_stride
     return {
@@ -85,7 +96,7 @@ def intermediates(plan, ws):
         "kp": plan.view(ws, "kp", torch.float32, (H, Nt, D)).cpu().numpy(),
         "vp": plan.view(ws, "vp", torch.float32, (H, Nt, D)).cpu().numpy(),
         "coarse": plan.view(ws, "coarse", torch.float32, (H, Nt, D)).cpu().numpy(),
-        "kt": plan.view(ws, "kt", torch.int16, (H, Nb, 64, D)).cpu(),
+        "kt": key_rows(plan.view(ws, "kt", torch.int16, (H, Nb, 64 * D)).cpu(), D, 32),
         "vt": plan.view(ws, "vt", torch.int16, (H, Nb, 2, D, 32)).cpu(),
         "probs": plan.view(ws, "scores", torch.float32, (H, Nt, ns)).cpu().numpy()[:, :, :Nt],
     }

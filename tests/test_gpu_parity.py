@@ -15,8 +15,8 @@ import torch
 import oracle
 import video_dit_block_amd as vsa
 from tests.gpu_helpers import (F32_MAX_ABS, F32_REL_L2, assert_close, check_all_heads_selection,
-                               check_dispatch_order, errors, intermediates, out_f64, require_gpu,
-                               run, say)
+                               check_dispatch_order, errors, intermediates, key_rows, out_f64,
+                               require_gpu, run, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -102,7 +102,8 @@ def full_check(w: Workload, x, sparsity, heads=None, check_tiles=True, plan=None
                     kl_ref[j, :len(idx)] = _lo_bits(x["k"][idx, h])
                     vl_ref[j, :len(idx)] = _lo_bits(x["v"][idx, h])
                 Nb = plan.num_blocks
-                kt_lo = plan.view(ws, "kt_lo", torch.int16, (H, Nb, 64, w.head_dim))[h].cpu()
+                kt_lo = key_rows(plan.view(ws, "kt_lo", torch.int16, (H, Nb, 64 * w.head_dim))
+                                 .cpu(), w.head_dim, 32)[h]
                 vt_lo = plan.view(ws, "vt_lo", torch.int16, (H, Nb, 2, w.head_dim, 32))[h].cpu()
                 assert torch.equal(kt_lo, kl_ref), f"K low parts head {h}"
                 vl_halves = vl_ref.transpose(1, 2)[:, :, cols].reshape(

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_helpers import (assert_close, check_all_heads_selection, errors, intermediates,
+from tests.gpu_helpers import (assert_close, check_all_heads_selection, errors, intermediates, key_rows,
                                oracle_prep, out_f64,
                                require_gpu, run, run_qk_prep, say)
 from workloads import AUDIO, COND, TEXT, WORKLOADS, Workload, make_inputs, make_qk_prep_inputs
@@ -28,7 +28,7 @@ def _gpu():
 def _check_key_codes(plan, ws, k32, g, h, D):
     """kt8/kscale of head h against the oracle's per-row quantisation."""
     H, Nt = plan.heads, plan.num_tiles
-    codes = plan.view(ws, "kt8", torch.uint8, (H, Nt, 64, D))[h].cpu().numpy()
+    codes = key_rows(plan.view(ws, "kt8", torch.uint8, (H, Nt, 64 * D)).cpu(), D, 64)[h].numpy()
     scale = plan.view(ws, "kscale", torch.float32, (H, Nt, 64))[h].cpu().numpy()
     perm = g.perm()
     want_c = np.zeros((Nt, 64, D), np.uint8)

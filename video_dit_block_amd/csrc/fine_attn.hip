@@ -457,17 +457,15 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   //   K half:   [KROWB/64 groups][32 keys][64 B]: chunks 4G..4G+3 of a key
   //             row; logical chunk c sits at (c ^ swz64(key)) in its group;
   //   V^T half: [D rows][64 B] (the 32 keys of the half), the same swizzle.
-  // DMA load number x (0..NW*KH_LOADS-1, or 0..NW*VH_LOADS-1, over all waves;
-  // 64 lanes x 16 B each)
-  // fills LDS chunks 64x..64x+63: K rows 16(x % 2) + lane/4 of group x/2,
-  // V^T rows 16x + lane/4.  The lane part of the source offset is the same
-  // for every load, the rest is uniform.
+  // Both halves are stored in memory in this order (the gather writes K
+  // halves group by group), so DMA load number x (0..NW*KH_LOADS-1, or
+  // 0..NW*VH_LOADS-1, over all waves; 64 lanes x 16 B each) reads bytes
+  // 1024x..1024x+1023 of the half and fills LDS chunks 64x..64x+63: K rows
+  // 16(x % 2) + lane/4 of group x/2, V^T rows 16x + lane/4.  The lane part of
+  // the source offset (the row and its swizzled chunk) is the same for every
+  // load, the rest is uniform.
   const int lane_sw = ((lane & 3) ^ ((lane >> 4) & 3)) << 4;
-  const int kbase = (lane >> 2) * KROWB + lane_sw;
-  // The same 16 rows further, less the 1 KB that the immediate offset adds.
-  const int kbase2 = kbase + 16 * KROWB - 1024;
-  static_assert(16 * KROWB >= 1024, "second lane offset is non-negative");
-  const int vbase = (lane >> 2) * 64 + lane_sw;
+  const int lbase = (lane >> 2) * 64 + lane_sw;
 // Block barrier without the workgroup fence of __syncthreads() and its cache
 // maintenance.  LDS reads are drained first (so no wave's pending read can
 // race the next DMA into that region); DMA completion is awaited explicitly
@@ -480,37 +478,29 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 // lanes 0..3).
 // Pad rows are zero in memory, so a loaded half holds no stale data; a half
 // without valid keys is neither loaded nor read.
-// With an even number of loads per wave, loads x and x + 1 (x even) fill the
-// two 16-row halves of one 64-byte group: they share an LDS base and an SGPR
-// offset, the second adding 1 KB to both addresses through the immediate
-// offset and the rest of its 16-row step through a second lane offset.
+// This wave's loads cover consecutive 1 KB of both memory and LDS: one LDS
+// base (M0) and one SGPR offset serve them all, and the instruction's
+// immediate offset, which the hardware adds to the global and to the LDS
+// address alike, steps through them.
 #define VSA_LOAD_KH(SLOT, J, B)                                                               \
   {                                                                                            \
     _Pragma("unroll") for (int p_ = 0; p_ < KPARTS; ++p_) {                                    \
-      if constexpr (KH_LOADS % 2 == 0) {                                                       \
-        _Pragma("unroll") for (int e = 0; e < KH_LOADS; e += 2) {                              \
-          const int x_ = w * KH_LOADS + e;                                                     \
-          char* const l_ = (SLOT) + p_ * KH_BYTES + x_ * 1024;                                 \
-          const int s_ = (J) * K_TILE + (B) * KH_BYTES + (x_ >> 1) * 64;                       \
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rkl : rk, (lds_void*)l_, 16, kbase, s_, \
-                                                   0, 0);                                      \
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rkl : rk, (lds_void*)l_, 16, kbase2,   \
-                                                   s_, 1024, 0);                               \
-        }                                                                                      \
-      } else {                                                                                 \
-        _Pragma("unroll") for (int e = 0; e < KH_LOADS; ++e) {                                 \
-          const int x_ = w * KH_LOADS + e;                                                     \
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(                                            \
-              p_ ? rkl : rk, (lds_void*)((SLOT) + p_ * KH_BYTES + x_ * 1024), 16, kbase,       \
-              (J) * K_TILE + (B) * KH_BYTES + (x_ & 1) * 16 * KROWB + (x_ >> 1) * 64, 0, 0);   \
-        }                                                                                      \
-      }                                                                                        \
+      char* const l_ = (SLOT) + p_ * KH_BYTES + w * KH_LOADS * 1024;                           \
+      const int s_ = (J) * K_TILE + (B) * KH_BYTES + w * KH_LOADS * 1024;                     \
+      VSA_KLOAD(0);                                                                            \
+      if (KH_LOADS > 1) VSA_KLOAD(1024);                                                       \
+      if (KH_LOADS > 2) VSA_KLOAD(2048);                                                       \
+      if (KH_LOADS > 3) VSA_KLOAD(3072);                                                       \
     }                                                                                          \
     if (QK8 && w < 2)                                                                          \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_void*)((SLOT) + KH_BYTES + 1024 * w),  \
                                                16, 16 * (lane & 3),                            \
                                                (J) * 256 + 128 * (B) + 64 * w, 0, 0);          \
   }
+// (the immediate offset must be a literal)
+#define VSA_KLOAD(OFF)                                                                         \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rkl : rk, (lds_void*)l_, 16, lbase, s_, OFF, 0)
+  static_assert(KH_LOADS * 1024 <= 4096, "immediate offsets of a K half fit in 12 bits");
 // Half B of V^T tile J into slot SLOT: VH_LOADS loads per wave and part.  A
 // V^T half is stored in LDS order, so this wave's loads cover consecutive
 // 1 KB of both memory and LDS: one LDS base (M0) and one SGPR offset serve
@@ -529,7 +519,7 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   }
 // (the immediate offset must be a literal)
 #define VSA_VLOAD(OFF)                                                                         \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rvl : rv, (lds_void*)l_, 16, vbase, s_, OFF, 0)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(p_ ? rvl : rv, (lds_void*)l_, 16, lbase, s_, OFF, 0)
   static_assert(VH_LOADS * 1024 <= 4096, "immediate offsets of a V^T half fit in 12 bits");
   // Swizzle of this lane's operand rows (key l32 of a K half, V^T row
   // 32n + l32; the latter does not depend on n).
@@ -924,6 +914,7 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
 #undef VSA_LOAD_VH
 #undef VSA_BARRIER
 #undef VSA_VLOAD
+#undef VSA_KLOAD
 
   if (!last) {
     if (active) {

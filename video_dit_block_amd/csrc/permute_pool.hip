@@ -8,7 +8,11 @@
 // One block per (head, tile).  A tile is one or two 64-slot blocks (64- or
 // 128-token tiles; block b holds slots 64b..64b+63).  For each block in turn
 // its 64 slots of q, k and v are staged in LDS (pad slots zero), then
-//   - k is written to Kt[h][tile][slot][d] (bf16),
+//   - k is written to Kt (bf16): per 64-slot block, each 32-slot half is
+//     stored in the order the fine kernel stages it in LDS, [group][32
+//     slots][64 bytes] with a group being 64 bytes of a key row (32 channels;
+//     64 channels of FP8 codes), so that every 1 KB DMA load of the fine
+//     kernel reads 1 KB of contiguous memory,
 //   - v is written transposed to Vt[h][tile][half][d][pos] (bf16, positions
 //     0-31 and 32-63 in two halves, so that the fine kernel can fetch a half
 //     tile as one block), the layout its P.V operand wants: inside each group of 16 slots the
@@ -199,10 +203,13 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
         kscale[tile_base * 64 + tid] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 0.0f;
       }
       __syncthreads();
+      // Codes in the Kt order: chunk c of 16 bytes is chunk c % 4 of slot
+      // 32 * half + (c / 4) % 32 in group (c / 128) % (D / 64) of 64 codes.
       uint8_t* dst = kt8 + tile_base * 64 * D;
       for (int c = tid; c < 64 * (D / 16); c += blockDim.x) {
-        const int slot = c / (D / 16);
-        const int d0 = (c - slot * (D / 16)) * 16;
+        const int g = (c >> 7) % (D / 64);
+        const int slot = 32 * ((c >> 7) / (D / 64)) + ((c >> 2) & 31);
+        const int d0 = 64 * g + 16 * (c & 3);
         const float inv = kinv[slot];
         u32x4 o;
 #pragma unroll
@@ -213,30 +220,39 @@ __global__ __launch_bounds__(384) void permute_pool_kernel(
           w = __builtin_amdgcn_cvt_pk_fp8_f32(to_f32(e[2]) * inv, to_f32(e[3]) * inv, w, true);
           o[j] = w;
         }
-        *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
+        *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(c) * 16) = o;
       }
     }
 
-    // Kt (and Qt with PREP): [slot][d] bf16, 16-byte chunks of 8 channels.
+    // Qt (with PREP): [slot][d] bf16; Kt: 16-byte chunk c (8 channels) is
+    // chunk c % 4 of slot 32 * half + (c / 4) % 32 in group (c / 128) % (D / 32)
+    // of 32 channels.  Consecutive threads write consecutive chunks.
     for (int x = PREP ? 0 : 1; x < (kt8 ? 1 : 2); ++x) {
       uint16_t* dst = (x == 0 ? prep.qt : kt) + tile_base * 64 * D;
       uint16_t* dlo = (x == 0 ? prep.qt_lo : kt_lo) + tile_base * 64 * D;
       for (int c = tid; c < 64 * (D / 8); c += blockDim.x) {
-        const int slot = c / (D / 8);
-        const int d0 = (c - slot * (D / 8)) * 8;
+        int slot, d0;
+        if (x == 0) {
+          slot = c / (D / 8);
+          d0 = (c - slot * (D / 8)) * 8;
+        } else {
+          slot = 32 * ((c >> 7) / (D / 32)) + ((c >> 2) & 31);
+          d0 = 32 * ((c >> 7) % (D / 32)) + 8 * (c & 3);
+        }
         const T* e = &lds[x][slot][d0];
         uint4 o;
         o.x = pack_bf16x2(to_f32(e[0]), to_f32(e[1]));
         o.y = pack_bf16x2(to_f32(e[2]), to_f32(e[3]));
         o.z = pack_bf16x2(to_f32(e[4]), to_f32(e[5]));
         o.w = pack_bf16x2(to_f32(e[6]), to_f32(e[7]));
-        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot) * D + d0) = o;
+        const size_t at = x == 0 ? static_cast<size_t>(slot) * D + d0 : static_cast<size_t>(c) * 8;
+        *reinterpret_cast<uint4*>(dst + at) = o;
         if constexpr (kLo) {
           o.x = pack_bf16x2_lo(e[0], e[1]);
           o.y = pack_bf16x2_lo(e[2], e[3]);
           o.z = pack_bf16x2_lo(e[4], e[5]);
           o.w = pack_bf16x2_lo(e[6], e[7]);
-          *reinterpret_cast<uint4*>(dlo + static_cast<size_t>(slot) * D + d0) = o;
+          *reinterpret_cast<uint4*>(dlo + at) = o;
         }
       }
     }
