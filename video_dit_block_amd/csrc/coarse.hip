@@ -14,7 +14,8 @@
 //
 // Three kernels:
 //   scores        64x64 output tile per block, 4x4 per thread, pooled rows
-//                 staged transposed in LDS in chunks of 32 channels;
+//                 staged transposed (and swizzled) in LDS in chunks of 32
+//                 channels;
 //   softmax_topk  one wave per (head, query tile): the row lives in
 //                 registers; an MSB-first bitwise search finds the k-th
 //                 largest key of each group (video tiles; reference tiles),
@@ -34,6 +35,7 @@ constexpr int kScoreTile = 64;
 constexpr int kMaxTiles = 4096;   // tiles per head the plan accepts
 constexpr int kDChunk = 32;
 constexpr int kPad = 4;
+static_assert(kDChunk == 32, "the staging swizzle pairs channel rows 16-31 with c4 >= 4");
 
 template <int D>
 __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qp,
@@ -58,29 +60,39 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
 
   for (int dc = 0; dc < D; dc += kDChunk) {
     // 64 rows x 32 channels = 512 float4 per operand; 2 per thread.
+    // Channel rows 16-31 of the staging hold their 64 entries with the
+    // column index XOR-ed with 8 (whole groups of 4 change places): a wave's
+    // transposing stores then meet each LDS bank at most twice (once with
+    // 64 banks) instead of four (two) times.
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int id = tid + e * 256;
       const int r = id / 8, c4 = id % 8;
+      const int rs = r ^ ((c4 >> 2) << 3);
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
       if (i0 + r < Nt) a = *reinterpret_cast<const float4*>(qh + static_cast<size_t>(i0 + r) * D + dc + 4 * c4);
       if (j0 + r < Nt) b = *reinterpret_cast<const float4*>(kh + static_cast<size_t>(j0 + r) * D + dc + 4 * c4);
-      qs[4 * c4 + 0][r] = a.x; qs[4 * c4 + 1][r] = a.y; qs[4 * c4 + 2][r] = a.z; qs[4 * c4 + 3][r] = a.w;
-      ks[4 * c4 + 0][r] = b.x; ks[4 * c4 + 1][r] = b.y; ks[4 * c4 + 2][r] = b.z; ks[4 * c4 + 3][r] = b.w;
+      qs[4 * c4 + 0][rs] = a.x; qs[4 * c4 + 1][rs] = a.y; qs[4 * c4 + 2][rs] = a.z; qs[4 * c4 + 3][rs] = a.w;
+      ks[4 * c4 + 0][rs] = b.x; ks[4 * c4 + 1][rs] = b.y; ks[4 * c4 + 2][rs] = b.z; ks[4 * c4 + 3][rs] = b.w;
     }
     __syncthreads();
     {
 #pragma clang fp contract(off)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int ci = (4 * ti) ^ (8 * hh), cj = (4 * tj) ^ (8 * hh);
 #pragma unroll 8
-      for (int dd = 0; dd < kDChunk; ++dd) {
-        const float4 a = *reinterpret_cast<const float4*>(&qs[dd][4 * ti]);
-        const float4 b = *reinterpret_cast<const float4*>(&ks[dd][4 * tj]);
-        const float av[4] = {a.x, a.y, a.z, a.w};
-        const float bv[4] = {b.x, b.y, b.z, b.w};
+        for (int d16 = 0; d16 < kDChunk / 2; ++d16) {
+          const int dd = 16 * hh + d16;
+          const float4 a = *reinterpret_cast<const float4*>(&qs[dd][ci]);
+          const float4 b = *reinterpret_cast<const float4*>(&ks[dd][cj]);
+          const float av[4] = {a.x, a.y, a.z, a.w};
+          const float bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+          for (int x = 0; x < 4; ++x)
 #pragma unroll
-          for (int y = 0; y < 4; ++y) acc[x][y] = acc[x][y] + av[x] * bv[y];
+            for (int y = 0; y < 4; ++y) acc[x][y] = acc[x][y] + av[x] * bv[y];
+        }
       }
     }
     __syncthreads();
