@@ -833,7 +833,8 @@ __global__ __launch_bounds__(64 * NW, kFineMinWaves<TIO>) void fine_attn_kernel(
   }
   // K half 0 and 1 and V^T half 0 of the first tile landed (and the query
   // and the running max and sums); the 4 NB loads of O may still be in
-  // flight (the compiler waits for them where O is first used).
+  // flight across the barrier (the compiler waits for them before the loop,
+  // which uses O).
   if (load_state)
     __builtin_amdgcn_s_waitcnt(kWaitVmO);
   else
