@@ -23,10 +23,10 @@ struct PermutePoolArgs {
   const int32_t* perm;          // [Nb][64]
   const int32_t* valid;         // [Nb] valid slots per block
   int H, Nt, D, bsh;
-  uint16_t *kt, *vt;            // [H][Nb][64][D], [H][Nb][2][D][32] bf16
+  uint16_t *kt, *vt;            // [H][Nb][2][D/32][32][32], [H][Nb][2][D][32] bf16
   float *qp, *kp, *vp;          // [H][Nt][D]
   QkPrepArgs prep;
-  uint8_t* kt8;                 // [H][Nb][64][D] E4M3 keys instead of kt, or null
+  uint8_t* kt8;                 // [H][Nb][2][D/64][32][64] E4M3 keys instead of kt, or null
   float* kscale;                // [H][Nb][64] per-key scale (with kt8)
   // fp32 I/O: low parts lo = bf16(x - bf16(x)) of the keys (layout of kt; not
   // with kt8) and values (layout of vt); null for bf16 I/O.
@@ -69,7 +69,7 @@ struct FineArgs {
   const void* gate;             // [L][H][D] io dtype
   void* out;                    // [L][H][D] io dtype
   bool io_f32;
-  const uint16_t* kt;           // [H][Nb][64][D] bf16
+  const uint16_t* kt;           // [H][Nb][2][D/32][32][32] bf16: per 32-key half, 32-channel groups
   const uint16_t* vt;           // [H][Nb][2][D][32] bf16
   const float* coarse;          // [H][Nt][D]
   const int32_t* perm;          // [Nb][64]
@@ -80,7 +80,7 @@ struct FineArgs {
   float* state;                 // running softmax state between chunks (nchunks > 1)
   int H, Nt, P, NV, listlen, D;
   int nchunks, chunk_tiles;
-  const uint8_t* kt8;           // [H][Nb][64][D] E4M3 keys: FP8 Q/K logits, or null
+  const uint8_t* kt8;           // [H][Nb][2][D/64][32][64] E4M3 keys: FP8 Q/K logits, or null
   const float* kscale;          // [H][Nb][64]
   int bsh, Pvis;
   const int32_t* order;         // [H][nchunks][Nt] dispatch order of query tiles (nchunks > 1)
