@@ -34,12 +34,13 @@
 //   - a key tile is staged in LDS as four half tiles (K keys 0-31, K keys
 //     32-63, V^T keys 0-31, V^T keys 32-63), one slot each, filled by direct
 //     global->LDS loads (buffer_load_dwordx4 ... lds, no register staging).
-//     The waves sync twice per tile: at the top, K of the tile has landed and
-//     the V^T slots take its V^T; after the two Q.K phases, V^T has landed
-//     and the K slots take the next tile's K.  Each load has two of the
-//     tile's four phases to land, and every wait is for all of the wave's
-//     loads (32 KB of LDS per workgroup: four two-wave or two four-wave
-//     workgroups per CU);
+//     A tile runs as four matrix phases (Q.K of half 0, P.V of the previous
+//     tile's half 1, Q.K of half 1, P.V of half 0), and the waves sync twice
+//     per tile, after the second and the fourth phase; at each sync the two
+//     slots the waves have just finished with take the next halves.  Each
+//     load has two of the four phases to land, and every wait is for all of
+//     the wave's loads (32 KB of LDS per workgroup: four two-wave or two
+//     four-wave workgroups per CU);
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so
 //     each lane holds one query column), online softmax in fp32 via exp2 with
 //     the 1/sqrt(D) scale folded into log2 units.  The exps of a half tile
@@ -56,11 +57,11 @@
 //   - LDS slots are made of 64-byte rows with XOR-swizzled 16-byte chunks,
 //     bank-conflict free for the MFMA operand reads; one per-lane offset
 //     serves every DMA load of a slot;
-//   - each key tile is taken in two 32-key halves, and the exp of one half
-//     is issued between the MFMAs of the other (Q.K of the second half, then
-//     P.V of the first), so softmax arithmetic and matrix work can overlap
-//     inside each wave; a half without valid keys is skipped, and the row's
-//     two lanes are combined only when its running max has to rise;
+//   - each key tile is taken in two 32-key halves, and a half's softmax is
+//     issued in two parts between the MFMAs of the neighbouring phases, so
+//     softmax arithmetic and matrix work overlap inside each wave; a half
+//     without valid keys is skipped, and the row's two lanes are combined
+//     only when its running max has to rise;
 //   - blocks are mapped to the 8 XCDs so that each XCD works through its own
 //     heads, head by head: the 32 CUs of an XCD sweep the same head's K/V;
 //   - fp32 I/O keeps fp32-level accuracy on the bf16 matrix cores: every
