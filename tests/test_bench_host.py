@@ -148,3 +148,26 @@ def test_cpu_baseline_pieces_report_host_and_stage_split():
     ref = oracle.forward_head(x["q"], x["k"], x["v"], x["gate"], g2,
                               oracle.topk_count(g2.NV, w.sparsity), 1)
     assert np.array_equal(r.out, ref.out) and np.array_equal(r.sel, ref.sel)
+
+
+def test_traffic_record_is_used_only_for_its_kernel_sources_and_schedule(tmp_path, monkeypatch):
+    """roofline.traffic comes from a committed counter record, and only while
+    the record matches the fine kernel's current sources (SHA-256), the
+    workload and the key-chunk schedule; anything else reports null."""
+    import json
+    rec = {"workload": "w", "bytes_per_launch": 123, "launches_per_forward": 4,
+           "key_chunk_tiles": 319,
+           "kernel_sources_sha256": bench.sources_digest(bench.FINE_SOURCES)}
+    path = tmp_path / "fine_attn_{workload}_traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    (tmp_path / "fine_attn_w_traffic.json").write_text(json.dumps(rec))
+    assert bench.load_traffic(4, "w", 319) == 123
+    assert bench.load_traffic(3, "w", 319) is None           # other launch count
+    assert bench.load_traffic(4, "w", 426) is None           # other chunk length
+    assert bench.load_traffic(4, "other", 319) is None       # no record for the workload
+    stale = dict(rec, kernel_sources_sha256="0" * 64)        # kernel changed since
+    (tmp_path / "fine_attn_w_traffic.json").write_text(json.dumps(stale))
+    assert bench.load_traffic(4, "w", 319) is None
+    (tmp_path / "fine_attn_w_traffic.json").write_text("not json")
+    assert bench.load_traffic(4, "w", 319) is None
+
